@@ -1,0 +1,131 @@
+"""fp64 CPU oracle for the SSD layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product library never links, loads
+or calls it, and it shares no code with the HIP path.
+
+It wraps ``ssd_oracle.c`` (plain C, fp64, sequential recurrence; see that
+file's header for the passages of the pages it follows) through ctypes.
+Inputs of any float dtype are upcast exactly to float64 (bf16 and fp32 values
+are exactly representable in fp64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB = os.path.join(_HERE, "libssd_oracle.so")
+_lib = None
+
+_F64P = ctypes.POINTER(ctypes.c_double)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_U8P = ctypes.POINTER(ctypes.c_uint8)
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (IEEE fp64: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-shared", "-fPIC", _SRC, "-o", tmp, "-lm",
+        ])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.ssd_oracle_fwd.restype = ctypes.c_int
+        lib.ssd_oracle_fwd.argtypes = [
+            ctypes.c_int64, _I64P, _I64P,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _U8P,
+            _F64P, _F64P, ctypes.c_int,
+        ]
+        lib.ssd_oracle_decode.restype = ctypes.c_int
+        lib.ssd_oracle_decode.argtypes = [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, ctypes.c_int,
+        ]
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a, typ=_F64P):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, init_state=None, cu_seqlens=None,
+            unit_mask=None, nthreads: int = 0):
+    """Sequential fp64 SSD forward.
+
+    Dense batch: x [b, L, H, P], dt [b, L, H], B/C [b, L, G, N].
+    Packed varlen: pass ``cu_seqlens`` (length nseq+1) with b == 1.
+    ``unit_mask`` [nseq, H] (bool) restricts the work to some (sequence, head)
+    pairs; outputs of skipped pairs are left at zero.
+    Returns (y [b, L, H, P] float64, final_state [nseq, H, P, N] float64).
+    """
+    x = _f64(x); dt = _f64(dt); A = _f64(A); B = _f64(B); C = _f64(C)
+    D = _f64(D); init_state = _f64(init_state)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, H) and B.shape == (b, L, G, N) and C.shape == B.shape
+    assert A.shape == (H,)
+    if cu_seqlens is None:
+        nseq = b
+        starts = np.arange(b, dtype=np.int64) * L
+        lens = np.full(b, L, dtype=np.int64)
+    else:
+        assert b == 1
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        nseq = cu.size - 1
+        starts = np.ascontiguousarray(cu[:-1])
+        lens = np.ascontiguousarray(cu[1:] - cu[:-1])
+        assert cu[0] == 0 and cu[-1] == L and np.all(lens >= 0)
+    if init_state is not None:
+        assert init_state.shape == (nseq, H, P, N)
+    mask = None
+    if unit_mask is not None:
+        mask = np.ascontiguousarray(np.asarray(unit_mask, dtype=np.uint8).reshape(nseq * H))
+    y = np.zeros((b, L, H, P), dtype=np.float64)
+    fin = np.zeros((nseq, H, P, N), dtype=np.float64)
+    rc = _load().ssd_oracle_fwd(
+        nseq, _ptr(starts, _I64P), _ptr(lens, _I64P), H, P, N, G,
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+        _ptr(mask, _U8P), _ptr(y), _ptr(fin), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_fwd failed with code {rc}")
+    return y, fin
+
+
+def ssd_decode(state, x, dt, A, B, C, D=None, nthreads: int = 0):
+    """One fp64 recurrent step.  state [b, H, P, N]; x [b, H, P]; dt [b, H];
+    B/C [b, G, N].  Returns (y [b, H, P], new_state [b, H, P, N]); the input
+    array is not modified."""
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    x = _f64(x); dt = _f64(dt); A = _f64(A); B = _f64(B); C = _f64(C); D = _f64(D)
+    b, H, P, N = st.shape
+    G = B.shape[1]
+    assert x.shape == (b, H, P) and dt.shape == (b, H) and B.shape == (b, G, N)
+    y = np.zeros((b, H, P), dtype=np.float64)
+    rc = _load().ssd_oracle_decode(b, H, P, N, G, _ptr(st), _ptr(x), _ptr(dt), _ptr(A),
+                                   _ptr(B), _ptr(C), _ptr(D), _ptr(y), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_decode failed with code {rc}")
+    return y, st
