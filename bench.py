@@ -1,0 +1,215 @@
+"""Benchmark of the SSD forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one ssd_chunk_scan_fwd call over one batch of the Mamba-2 2.7B layer
+shape (batch 4, L 8192, 80 heads x 64, state 128, 1 group, chunk 256, bf16
+x/B/C, fp32 dt/A/D/state, random fp32 initial state).  Inputs are seeded
+synthetic data resident in HBM before timing starts.  Prints one JSON line.
+
+The roofline object reports the fused forward kernel against HBM bandwidth
+(its algorithmic bytes are the compulsory traffic; see the design doc for the
+per-token figures) and, in "mfma", its algorithmic bf16 MFMA rate.  The
+"cpu_baseline" is the fp64 oracle timed on this host's cores over the whole
+workload.  A decode line for the b256 H80 P64 N128 single-token step is
+included under "decode".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FWD_INDEX = 2                  # Mamba-2 2.7B layer shape
+DEC_INDEX = 4                  # decode, b256
+
+
+def fwd_algorithmic(w):
+    """Algorithmic bytes and MFMA flops of one forward pass.
+
+    Bytes: the compulsory HBM traffic -- read x, dt, B, C, the initial state,
+    write y and the final state (A, D negligible).
+    Flops per (token, head): the causal half of the diagonal block
+    2*(Q+1)/2*P, the chunk-state formation 2*N*P and the state read-out
+    2*N*P; per (token, group): the causal half of C B^T, 2*(Q+1)/2*N."""
+    b, L, H, P, N, G, Q = (w["batch"], w["seqlen"], w["nheads"], w["headdim"], w["dstate"],
+                           w["ngroups"], w["chunk"])
+    tok = b * L
+    io = 2
+    byts = tok * (H * P * io * 2 + H * 4 + G * N * io * 2) + 2 * b * H * P * N * 4
+    flops = tok * H * (2 * (Q + 1) / 2 * P + 4 * N * P) + tok * G * (2 * (Q + 1) / 2 * N)
+    return float(byts), float(flops)
+
+
+def dec_algorithmic(w):
+    b, H, P, N, G = w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"]
+    return float(8 * b * H * P * N + b * H * P * 2 * 2 + b * H * 4 + 2 * b * G * N * 2)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("ssd_fwd_kernel.h", "ssd_device.h", "ssd_fwd_launch.h"):
+        with open(os.path.join(ROOT, "selective_state_space_71_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), or
+    None when absent or taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "fwd_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the SSD forward shards by (sequence, head) "
+              "with no exchange, so N GPUs run N independent copies; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_71_amd import ssd
+    from selective_state_space_71_amd import workloads as wl
+
+    ssd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[FWD_INDEX]
+    inp = wl.workload_inputs(FWD_INDEX)
+
+    def to_dev(a, bf16):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x, B, C = (to_dev(inp[k], True) for k in ("x", "B", "C"))
+    dt, A, D, h0 = (to_dev(inp[k], False) for k in ("dt", "A", "D", "init_state"))
+    y = torch.empty_like(x)
+    fin = torch.empty_like(h0)
+    y, fin = ssd.chunk_scan_fwd(x, dt, A, B, C, D, chunk_len=w["chunk"], init_state=h0, y=y,
+                                final_state=fin)
+    ws = ssd.chunk_scan_fwd.last_workspace
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssd.chunk_scan_fwd(x, dt, A, B, C, D, chunk_len=w["chunk"], init_state=h0, y=y,
+                           final_state=fin, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert ssd.check_workspace(ws) == 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    ms_total = ev[0].elapsed_time(ev[-1])
+    ms_step = ms_total / args.steps
+    assert ssd.check_workspace(ws) == 0
+    tokens = w["batch"] * w["seqlen"]
+    byts, flops = fwd_algorithmic(w)
+    ms_launch = float(np.mean(per))
+    gbs = byts / (ms_launch * 1e-3) / 1e9
+    tfl = flops / (ms_launch * 1e-3) / 1e12
+    print(f"[bench] fwd {ms_step * 1e3:.1f} us/step (median {np.median(per) * 1e3:.1f}), "
+          f"{gbs:.0f} GB/s alg, {tfl:.1f} TFLOP/s alg", file=sys.stderr, flush=True)
+    out = {
+        "metric": "SSD fwd tokens/s at Mamba-2 2.7B layer shape, L=8192; % bf16 MFMA peak",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mamba2_2p7b_layer: batch 4, L 8192, H 80, P 64, N 128, G 1, "
+                               "chunk 256, bf16 x/B/C, fp32 dt/A/D/state, init state N(0,0.1)",
+                   "global_batch": w["batch"], "seq_len": w["seqlen"], "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(),
+                     "kernel": "ssd_fwd_kernel (plus the tiny schedule kernel in the same launch)",
+                     "alg_bytes_per_launch": byts, "launch_us": ms_launch * 1e3},
+        "mfma": {"achieved": tfl, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tfl / BF16_PEAK_TFLOPS, "alg_flops_per_launch": flops},
+        "wall_s_timed": wall,
+    }
+
+    if not args.no_decode:
+        wd = wl.WORKLOADS[DEC_INDEX]
+        di = wl.workload_inputs(DEC_INDEX)
+        st = to_dev(di["state"], False)
+        dx, dB, dC = (to_dev(di[k], True) for k in ("x", "B", "C"))
+        ddt, dA, dD = (to_dev(di[k], False) for k in ("dt", "A", "D"))
+        dy = torch.empty_like(dx)
+        for _ in range(3):
+            ssd.decode_step(st, dx, ddt, dA, dB, dC, dD, y=dy)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrep = 50
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(nrep):
+            ssd.decode_step(st, dx, ddt, dA, dB, dC, dD, y=dy)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / nrep * 1e3
+        db = dec_algorithmic(wd)
+        out["decode"] = {"workload": "decode: batch 256, H 80, P 64, N 128, G 1, fp32 state",
+                         "tokens_per_s": wd["batch"] / (us * 1e-6), "us_per_step": us,
+                         "achieved_gbs": db / (us * 1e-6) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+                         "frac": db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del st, dx, dB, dC, ddt, dA, dD, dy
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        x64 = wl.as_f64(inp["x"], "bf16")
+        B64 = wl.as_f64(inp["B"], "bf16")
+        C64 = wl.as_f64(inp["C"], "bf16")
+        t = time.perf_counter()
+        oracle.ssd_fwd(x64, inp["dt"], inp["A"], B64, C64, inp["D"], init_state=inp["init_state"],
+                       nthreads=threads)
+        cpu_s = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": tokens / cpu_s, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "the whole workload (4 x 8192 tokens, 80 heads), fp64 "
+                                         f"sequential recurrence, {cpu_s:.1f} s"}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) SSD layer library, libssd.so.
+ *
+ * The layer is the selective state-space recurrence with a scalar decay per
+ * head, which the Mamba-2 papers call structured state-space duality (SSD).
+ * For every sequence, head h (group g = h / (nheads/ngroups)) and token t:
+ *
+ *     abar_t = exp(dt[t,h] * A[h])
+ *     h_t    = abar_t * h_{t-1} + dt[t,h] * x[t,h,:] (outer) B[t,g,:]     (P x N)
+ *     y[t,h] = h_t * C[t,g,:] + D[h] * x[t,h,:]
+ *
+ * Sources (cited by page title and section):
+ *   - "Mamba-2는 왜 Transformer와 닮았는가: SSD로 다시 읽는 SSM" (bdev.io), the
+ *     problem section: the recurrence h_t = A_t h_{t-1} + B_t x_t,
+ *     y_t = C_t^T h_t.
+ *   - "20.1 상태 공간 모델 (SSM)" textbook chapter (sungeuns.github.io),
+ *     section 1: zero-order-hold Abar = exp(dt A) and Bbar ~= dt B, skip D;
+ *     section 3: A restricted to a scalar times identity (one scalar per head);
+ *     section 5: the state is updated before the output is read out.
+ *   - "Transformers are SSMs Review" (dimensionstp.github.io), section
+ *     3-2(4): the chunked SSD algorithm (quadratic masked form inside a chunk,
+ *     chunk-boundary states passed between chunks); section 3-2(6): packed
+ *     variable-length batches cut the state at sequence boundaries.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless noted, row-major and contiguous.
+ *     The caller owns every buffer; the library allocates nothing, keeps no
+ *     mutable global state and is reentrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns before it completes.  Asynchronous device faults show
+ *     up at the caller's next synchronisation.
+ *   - Arguments are validated synchronously before anything is launched; an
+ *     invalid call returns a status and launches nothing.  No C++ exception
+ *     crosses the ABI.
+ *   - Preconditions that are documented but not checked: inputs are finite;
+ *     cu_seqlens[0] == 0, cu_seqlens is non-decreasing and its last entry is
+ *     seqlen.  Non-finite values stay inside their own sequence.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_PTR = 1,     /* a required pointer is NULL                         */
+    SSD_ERR_SHAPE = 2,        /* a dimension is <= 0 or inconsistent                 */
+    SSD_ERR_DTYPE = 3,        /* io dtype is not SSD_F32 or SSD_BF16                 */
+    SSD_ERR_UNSUPPORTED = 4,  /* headdim/dstate/chunk_len combination not built      */
+    SSD_ERR_ALIGNMENT = 5,    /* a pointer is not 16-byte aligned (workspace: 256)   */
+    SSD_ERR_ALIAS = 6,        /* an output overlaps an input it must not overlap     */
+    SSD_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than the size query says  */
+    SSD_ERR_HIP = 8,          /* the HIP runtime reported an error at launch         */
+    SSD_ERR_DEVICE = 9        /* a kernel reported an internal failure (see below)   */
+} ssd_status_t;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;  /* dtype of x, B, C, y */
+
+typedef struct {
+    int32_t batch;    /* dense batch size; 1 for a packed varlen batch               */
+    int32_t seqlen;   /* tokens per batch row (varlen: total packed tokens)          */
+    int32_t nheads;   /* H                                                           */
+    int32_t headdim;  /* P, channels per head                                        */
+    int32_t dstate;   /* N, state size per channel                                   */
+    int32_t ngroups;  /* G, groups sharing B and C; nheads % ngroups == 0            */
+    int32_t nseq;     /* number of sequences: == batch when cu_seqlens is NULL       */
+} ssd_dims_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *ssd_status_string(ssd_status_t status);
+
+/* SSD_ABI_VERSION of the built library. */
+int32_t ssd_abi_version(void);
+
+/*
+ * Bytes of device workspace ssd_chunk_scan_fwd needs for these dimensions,
+ * chunk length and io dtype, or 0 when the arguments are invalid.  The
+ * workspace holds the chunk schedule, per-(sequence, head) progress flags and
+ * the fp32 chunk-boundary states; it needs no initialisation by the caller.
+ */
+size_t ssd_chunk_scan_fwd_workspace_size(const ssd_dims_t *dims, int32_t chunk_len,
+                                         ssd_dtype_t io_dtype);
+
+/*
+ * Chunked SSD forward pass (the chunked algorithm of "Transformers are SSMs
+ * Review", section 3-2(4)): per chunk of chunk_len tokens the output is the
+ * masked quadratic form (C B^T o L) dt x, plus the incoming chunk-boundary
+ * state read out through C, plus D x; the boundary states are passed from
+ * chunk to chunk in fp32.  The result equals the recurrence above; only the
+ * evaluation order (and so the rounding) differs, and it does not depend on
+ * chunk_len beyond rounding.
+ *
+ *   dims        host pointer.  Dense batch: cu_seqlens == NULL, nseq == batch.
+ *               Packed varlen: batch == 1, cu_seqlens != NULL, nseq >= 1.
+ *   io_dtype    dtype of x, B, C and y.  Arithmetic: fp32 accumulation and
+ *               state; SSD_BF16 contractions run on bf16 MFMA, SSD_F32 on
+ *               fp32 MFMA.
+ *   chunk_len   64, 128 or 256.
+ *   x           [batch, seqlen, nheads, headdim]  io
+ *   dt          [batch, seqlen, nheads] fp32, the final (positive) step size
+ *   A           [nheads] fp32, the scalar decay rate per head (expected <= 0;
+ *               0 is allowed and gives linear attention)
+ *   B, C        [batch, seqlen, ngroups, dstate]  io
+ *   D           [nheads] fp32, or NULL for no skip term
+ *   init_state  [nseq, nheads, headdim, dstate] fp32, or NULL for zeros.
+ *               It may be the same buffer as final_state (in-place resume).
+ *   cu_seqlens  [nseq + 1] int32 device offsets of the packed sequences, or
+ *               NULL.  The state restarts from init_state (or zero) at every
+ *               sequence start.  nseq <= 65536.
+ *   y           [batch, seqlen, nheads, headdim] io, output; must not overlap
+ *               any input.
+ *   final_state [nseq, nheads, headdim, dstate] fp32 output, or NULL.
+ *   workspace   device buffer of at least workspace_bytes >=
+ *               ssd_chunk_scan_fwd_workspace_size(...) bytes, 256-byte
+ *               aligned, not used by another call in flight.
+ *   stream      hipStream_t, or NULL for the default stream.
+ *
+ * Supported sizes: headdim in {16, 32, 64}; dstate in {16, 32, 64, 128};
+ * chunk_len in {64, 128, 256}; combinations whose chunk tiles do not fit in
+ * the 160 KB of LDS of a gfx950 compute unit return SSD_ERR_UNSUPPORTED.
+ * x, y, B, C, dt, D and the states must be 16-byte aligned.
+ */
+ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
+                                int32_t chunk_len,
+                                const void *x, const float *dt, const float *A,
+                                const void *B, const void *C, const float *D,
+                                const float *init_state, const int32_t *cu_seqlens,
+                                void *y, float *final_state,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Reads the device-side failure word of a workspace after a forward call
+ * (synchronises `stream`).  Returns SSD_OK, or SSD_ERR_DEVICE when a chunk
+ * waited too long for its predecessor's state (the outputs of that call are
+ * then invalid), or SSD_ERR_HIP.  Meant for tests and diagnostics.
+ */
+ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream);
+
+/*
+ * One recurrent decode step for a single new token per sequence, updating
+ * the state in place (constant-size state per generated token, "Mamba-2는
+ * 왜 Transformer와 닮았는가", the problem section):
+ *     state = exp(dt A) state + dt x (outer) B;   y = state C + D x.
+ *
+ *   dims     host pointer; batch, nheads, headdim, dstate, ngroups are used
+ *            (seqlen and nseq are ignored).
+ *   state    [batch, nheads, headdim, dstate] fp32, read and written in place
+ *   x        [batch, nheads, headdim] io
+ *   dt       [batch, nheads] fp32
+ *   A, D     [nheads] fp32 (D may be NULL)
+ *   B, C     [batch, ngroups, dstate] io
+ *   y        [batch, nheads, headdim] io output; must not overlap the inputs.
+ *
+ * Supported sizes: headdim >= 1, dstate in {16, 32, 64, 128, 256}.
+ */
+ssd_status_t ssd_decode_step(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
+                             float *state, const void *x, const float *dt,
+                             const float *A, const void *B, const void *C,
+                             const float *D, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,440 @@
+// ssd_api.hip -- host side of libssd.so: argument validation, workspace
+// layout, the chunk-schedule kernel, the decode kernel and the C ABI.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/ssd.h"
+#include "ssd_device.h"
+#include "ssd_fwd_kernel.h"
+
+namespace ssd {
+bool fwd_dispatch_bf16(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
+                       bool launch, hipError_t *err);
+bool fwd_dispatch_f32(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
+                      bool launch, hipError_t *err);
+
+// ---------------------------------------------------------------------------
+// Chunk schedule.  Every (sequence, chunk index) pair becomes one entry
+// {seq, chunk index in seq, first token, length}.  Entries are ordered by
+// chunk index first and sequence second, so the predecessor of an entry
+// (same sequence, previous chunk) always has a smaller index; the forward
+// kernel hands out work in this order.  The kernel also clears the ticket,
+// the error word and the per-(sequence, head) progress flags, and writes the
+// final state of empty packed sequences (the initial state, or zero).
+struct PrepParams {
+    const int *cu_seqlens;  // null for a dense batch
+    int batch, seqlen, nseq, H, Q;
+    int state_elems;        // P * N
+    int4 *chunks;
+    int *n_chunks;
+    int *ticket;
+    int *error;
+    int *flags;
+    int *seq_chunk_start;   // [nseq + 1] scratch (packed batches)
+    const float *init_state;
+    float *final_state;
+};
+
+__global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
+    const int tid = threadIdx.x;
+    const int Q = p.Q;
+    for (int u = tid; u < p.nseq * p.H; u += 256) p.flags[u] = 0;
+    if (tid == 0) {
+        *p.ticket = 0;
+        *p.error = 0;
+    }
+    if (p.cu_seqlens == nullptr) {
+        const int nc = (p.seqlen + Q - 1) / Q;
+        const int total = nc * p.batch;
+        if (tid == 0) *p.n_chunks = total;
+        for (int e = tid; e < total; e += 256) {
+            const int c = e / p.batch;
+            const int s = e - c * p.batch;
+            const int start = c * Q;
+            const int len = min(Q, p.seqlen - start);
+            p.chunks[e] = make_int4(s, c, s * p.seqlen + start, len);
+        }
+        return;
+    }
+    // packed batch: chunk counts and their running sum over sequences
+    if (tid == 0) {
+        int acc = 0;
+        for (int s = 0; s < p.nseq; ++s) {
+            p.seq_chunk_start[s] = acc;
+            const int len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
+            acc += (len > 0) ? (len + Q - 1) / Q : 0;
+        }
+        p.seq_chunk_start[p.nseq] = acc;
+        *p.n_chunks = acc;
+    }
+    __syncthreads();
+    const int total = p.seq_chunk_start[p.nseq];
+    for (int f = tid; f < total; f += 256) {
+        int lo = 0, hi = p.nseq - 1;  // last s with seq_chunk_start[s] <= f
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.seq_chunk_start[mid] <= f) lo = mid; else hi = mid - 1;
+        }
+        const int s = lo;
+        const int c = f - p.seq_chunk_start[s];
+        // position in chunk-index-major order
+        int idx = 0;
+        for (int t = 0; t < p.nseq; ++t) {
+            const int nct = p.seq_chunk_start[t + 1] - p.seq_chunk_start[t];
+            idx += min(nct, c) + ((t < s && nct > c) ? 1 : 0);
+        }
+        const int start = p.cu_seqlens[s] + c * Q;
+        const int len = min(Q, p.cu_seqlens[s + 1] - start);
+        p.chunks[idx] = make_int4(s, c, start, len);
+    }
+    if (p.final_state) {
+        for (int s = 0; s < p.nseq; ++s) {
+            if (p.cu_seqlens[s + 1] > p.cu_seqlens[s]) continue;
+            const long long base = (long long)s * p.H * p.state_elems;
+            for (long long k = tid; k < (long long)p.H * p.state_elems; k += 256)
+                p.final_state[base + k] = p.init_state ? p.init_state[base + k] : 0.f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one workgroup per (batch row, head).  Each thread owns four
+// consecutive state columns (one 16-byte vector) of several state rows; the
+// P x N fp32 state is streamed once (read, updated, written back in place by
+// the same lane, so there is no read-after-write hazard), and the per-row
+// read-out C . h is reduced across the N/4 lanes that share the row.
+struct DecodeParams {
+    float *state;
+    const void *x;
+    const float *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;
+    void *y;
+    int H, G, P;
+};
+
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void ssd_decode_kernel(DecodeParams p) {
+    constexpr int C4 = N / 4;          // lanes per state row
+    constexpr int RPP = 256 / C4;      // rows per pass of the workgroup
+    constexpr int UNR = (64 / RPP) > 0 ? (64 / RPP) : 1;  // passes kept in flight
+    const int u = blockIdx.x;
+    const int b = u / p.H;
+    const int h = u - b * p.H;
+    const int g = h / (p.H / p.G);
+    const int tid = threadIdx.x;
+    const int c4 = tid % C4;
+    const int r0 = tid / C4;
+    const IO *Bp = reinterpret_cast<const IO *>(p.B) + ((long long)b * p.G + g) * N + 4 * c4;
+    const IO *Cp = reinterpret_cast<const IO *>(p.C) + ((long long)b * p.G + g) * N + 4 * c4;
+    float bv[4], cv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { bv[k] = to_f32(Bp[k]); cv[k] = to_f32(Cp[k]); }
+    const float d = p.dt[u];
+    const float abar = __expf(d * p.A[h]);
+    const float Dh = p.D ? p.D[h] : 0.f;
+    const IO *xp = reinterpret_cast<const IO *>(p.x) + (long long)u * p.P;
+    IO *yp = reinterpret_cast<IO *>(p.y) + (long long)u * p.P;
+    f32x4 *st = reinterpret_cast<f32x4 *>(p.state + (long long)u * p.P * N);
+    for (int base = 0; base < p.P; base += RPP * UNR) {
+        f32x4 hv[UNR];
+        float xv[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const int row = base + k * RPP + r0;
+            if (row < p.P) {
+                hv[k] = __builtin_nontemporal_load(st + (long long)row * C4 + c4);
+                xv[k] = to_f32(xp[row]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const int row = base + k * RPP + r0;
+            float part = 0.f;
+            if (row < p.P) {
+                const float dx = d * xv[k];
+                f32x4 nv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    nv[e] = abar * hv[k][e] + dx * bv[e];
+                    part += nv[e] * cv[e];
+                }
+                __builtin_nontemporal_store(nv, st + (long long)row * C4 + c4);
+            }
+#pragma unroll
+            for (int off = C4 / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+            if (row < p.P && c4 == 0) yp[row] = from_f32<IO>(part + Dh * xv[k]);
+        }
+    }
+}
+
+template <typename IO>
+static bool decode_launch(int N, const DecodeParams &prm, unsigned grid, hipStream_t st) {
+    switch (N) {
+    case 16: hipLaunchKernelGGL((ssd_decode_kernel<IO, 16>), dim3(grid), dim3(256), 0, st, prm); return true;
+    case 32: hipLaunchKernelGGL((ssd_decode_kernel<IO, 32>), dim3(grid), dim3(256), 0, st, prm); return true;
+    case 64: hipLaunchKernelGGL((ssd_decode_kernel<IO, 64>), dim3(grid), dim3(256), 0, st, prm); return true;
+    case 128: hipLaunchKernelGGL((ssd_decode_kernel<IO, 128>), dim3(grid), dim3(256), 0, st, prm); return true;
+    case 256: hipLaunchKernelGGL((ssd_decode_kernel<IO, 256>), dim3(grid), dim3(256), 0, st, prm); return true;
+    default: return false;
+    }
+}
+
+}  // namespace ssd
+
+// ===========================================================================
+// C ABI
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range rng(const void *p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == 0 || b.lo == 0 || a.hi == a.lo || b.hi == b.lo) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct WsLayout {
+    size_t flags, chunks, scratch, state, total;
+    long long max_entries;
+};
+
+// Workspace: [0,256) ticket / error / entry count; per-(sequence, head)
+// flags; chunk table; packed-batch scratch; fp32 boundary-state buffer.
+bool ws_layout(const ssd_dims_t &d, int Q, bool varlen, WsLayout *w) {
+    const long long nc = ((long long)d.seqlen + Q - 1) / Q;
+    w->max_entries = varlen ? nc + d.nseq : nc * d.batch;
+    w->flags = 256;
+    w->chunks = align_up(w->flags + (size_t)d.nseq * d.nheads * 4, 256);
+    w->scratch = align_up(w->chunks + (size_t)w->max_entries * 16, 256);
+    w->state = align_up(w->scratch + (size_t)(d.nseq + 1) * 4, 256);
+    w->total = align_up(w->state + (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4, 256);
+    return true;
+}
+
+bool dims_ok(const ssd_dims_t &d) {
+    return d.batch >= 1 && d.seqlen >= 1 && d.nheads >= 1 && d.headdim >= 1 && d.dstate >= 1 &&
+           d.ngroups >= 1 && d.nseq >= 1 && d.nheads % d.ngroups == 0;
+}
+
+ssd_status_t fwd_shape_check(const ssd_dims_t *dims, int32_t chunk_len, ssd_dtype_t io, bool varlen) {
+    if (!dims) return SSD_ERR_NULL_PTR;
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
+    const ssd_dims_t &d = *dims;
+    if (!dims_ok(d)) return SSD_ERR_SHAPE;
+    if (varlen) {
+        if (d.batch != 1 || d.nseq > 65536) return SSD_ERR_SHAPE;
+    } else if (d.nseq != d.batch) {
+        return SSD_ERR_SHAPE;
+    }
+    if (chunk_len != 64 && chunk_len != 128 && chunk_len != 256) return SSD_ERR_UNSUPPORTED;
+    ssd::FwdParams dummy{};
+    hipError_t e = hipSuccess;
+    const bool built = (io == SSD_BF16)
+                           ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, dummy, 0, nullptr, false, &e)
+                           : ssd::fwd_dispatch_f32(d.headdim, d.dstate, chunk_len, dummy, 0, nullptr, false, &e);
+    if (!built) return SSD_ERR_UNSUPPORTED;
+    // sizes must stay within the kernels' 32-bit schedule fields
+    const long long tokens = (long long)d.batch * d.seqlen;
+    if (tokens > INT_MAX / 2) return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(ssd_status_t s) {
+    switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL_PTR: return "SSD_ERR_NULL_PTR: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: invalid or inconsistent dimensions";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown io dtype";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: headdim/dstate/chunk_len combination not built";
+    case SSD_ERR_ALIGNMENT: return "SSD_ERR_ALIGNMENT: pointer not sufficiently aligned";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output overlaps an input";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime error";
+    case SSD_ERR_DEVICE: return "SSD_ERR_DEVICE: a kernel reported an internal failure";
+    }
+    return "SSD status: unknown code";
+}
+
+int32_t ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+size_t ssd_chunk_scan_fwd_workspace_size(const ssd_dims_t *dims, int32_t chunk_len, ssd_dtype_t io) {
+    if (!dims) return 0;
+    // the size query does not know whether cu_seqlens will be passed: accept
+    // either reading of the dims and size for the larger (packed) schedule
+    if (fwd_shape_check(dims, chunk_len, io, true) != SSD_OK &&
+        fwd_shape_check(dims, chunk_len, io, false) != SSD_OK)
+        return 0;
+    WsLayout packed{}, dense{};
+    ws_layout(*dims, chunk_len, true, &packed);
+    ws_layout(*dims, chunk_len, false, &dense);
+    return packed.total > dense.total ? packed.total : dense.total;
+}
+
+ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
+                                const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, const float *init_state,
+                                const int32_t *cu_seqlens, void *y, float *final_state,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    const bool varlen = cu_seqlens != nullptr;
+    ssd_status_t st = fwd_shape_check(dims, chunk_len, io, varlen);
+    if (st != SSD_OK) return st;
+    const ssd_dims_t &d = *dims;
+    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_PTR;
+    if (!workspace) return SSD_ERR_WORKSPACE;
+    const void *al16[] = {x, dt, A, B, C, D, init_state, y, final_state};
+    for (const void *p : al16)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
+    if (!aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
+
+    const size_t E = (io == SSD_BF16) ? 2 : 4;
+    const size_t tokens = (size_t)d.batch * d.seqlen;
+    const size_t nx = tokens * d.nheads * d.headdim * E;
+    const size_t nbc = tokens * d.ngroups * d.dstate * E;
+    const size_t nstate = (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4;
+    const Range ry = rng(y, nx);
+    const Range rx = rng(x, nx), rdt = rng(dt, tokens * d.nheads * 4), rA = rng(A, (size_t)d.nheads * 4);
+    const Range rB = rng(B, nbc), rC = rng(C, nbc), rD = rng(D, D ? (size_t)d.nheads * 4 : 0);
+    const Range ri = rng(init_state, init_state ? nstate : 0), rf = rng(final_state, final_state ? nstate : 0);
+    const Range rcu = rng(cu_seqlens, cu_seqlens ? (size_t)(d.nseq + 1) * 4 : 0);
+    WsLayout w{};
+    ws_layout(d, chunk_len, varlen, &w);
+    if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+    const Range rw = rng(workspace, w.total);
+    for (Range r : {rx, rdt, rA, rB, rC, rD, ri, rf, rcu, rw})
+        if (overlap(ry, r)) return SSD_ERR_ALIAS;
+    for (Range r : {rx, rdt, rA, rB, rC, rD, rcu, rw})
+        if (overlap(rf, r)) return SSD_ERR_ALIAS;   // final_state may equal init_state
+    if (final_state && init_state && overlap(rf, ri) && rf.lo != ri.lo) return SSD_ERR_ALIAS;
+    for (Range r : {rx, rdt, rA, rB, rC, rD, ri, rcu})
+        if (overlap(rw, r)) return SSD_ERR_ALIAS;
+    if (w.max_entries * d.nheads > INT_MAX) return SSD_ERR_SHAPE;
+
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ssd::PrepParams pp{};
+    pp.cu_seqlens = cu_seqlens;
+    pp.batch = d.batch;
+    pp.seqlen = d.seqlen;
+    pp.nseq = d.nseq;
+    pp.H = d.nheads;
+    pp.Q = chunk_len;
+    pp.state_elems = d.headdim * d.dstate;
+    pp.chunks = reinterpret_cast<int4 *>(ws + w.chunks);
+    pp.n_chunks = reinterpret_cast<int *>(ws + 8);
+    pp.ticket = reinterpret_cast<int *>(ws + 0);
+    pp.error = reinterpret_cast<int *>(ws + 4);
+    pp.flags = reinterpret_cast<int *>(ws + w.flags);
+    pp.seq_chunk_start = reinterpret_cast<int *>(ws + w.scratch);
+    pp.init_state = init_state;
+    pp.final_state = final_state;
+    hipLaunchKernelGGL(ssd::ssd_prep_kernel, dim3(1), dim3(256), 0, s, pp);
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+
+    ssd::FwdParams fp{};
+    fp.x = x;
+    fp.dt = dt;
+    fp.A = A;
+    fp.B = B;
+    fp.C = C;
+    fp.D = D;
+    fp.init_state = init_state;
+    fp.y = y;
+    fp.state = final_state ? final_state : reinterpret_cast<float *>(ws + w.state);
+    fp.chunks = pp.chunks;
+    fp.n_chunks = pp.n_chunks;
+    fp.ticket = pp.ticket;
+    fp.flags = pp.flags;
+    fp.error = pp.error;
+    fp.H = d.nheads;
+    fp.G = d.ngroups;
+    const unsigned grid = (unsigned)(w.max_entries * d.nheads);
+    fp.grid = grid;
+    hipError_t err = hipSuccess;
+    const bool ok = (io == SSD_BF16)
+                        ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, fp, grid, s, true, &err)
+                        : ssd::fwd_dispatch_f32(d.headdim, d.dstate, chunk_len, fp, grid, s, true, &err);
+    if (!ok) return SSD_ERR_UNSUPPORTED;
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream) {
+    if (!workspace) return SSD_ERR_WORKSPACE;
+    int word = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return SSD_ERR_HIP;
+    if (hipMemcpy(&word, static_cast<const char *>(workspace) + 4, sizeof(int), hipMemcpyDeviceToHost) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
+    return word ? SSD_ERR_DEVICE : SSD_OK;
+}
+
+ssd_status_t ssd_decode_step(const ssd_dims_t *dims, ssd_dtype_t io, float *state, const void *x,
+                             const float *dt, const float *A, const void *B, const void *C,
+                             const float *D, void *y, void *stream) {
+    if (!dims) return SSD_ERR_NULL_PTR;
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
+    const ssd_dims_t &d = *dims;
+    if (d.batch < 1 || d.nheads < 1 || d.headdim < 1 || d.dstate < 1 || d.ngroups < 1 ||
+        d.nheads % d.ngroups != 0)
+        return SSD_ERR_SHAPE;
+    const int N = d.dstate;
+    if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return SSD_ERR_UNSUPPORTED;
+    if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_PTR;
+    const void *al16[] = {state, x, dt, A, B, C, D, y};
+    for (const void *p : al16)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
+    const size_t E = (io == SSD_BF16) ? 2 : 4;
+    const size_t units = (size_t)d.batch * d.nheads;
+    if (units > (size_t)INT_MAX) return SSD_ERR_SHAPE;
+    const Range rs = rng(state, units * d.headdim * N * 4);
+    const Range rx = rng(x, units * d.headdim * E), ry = rng(y, units * d.headdim * E);
+    const Range rdt = rng(dt, units * 4), rA = rng(A, (size_t)d.nheads * 4);
+    const Range rB = rng(B, (size_t)d.batch * d.ngroups * N * E), rC = rng(C, (size_t)d.batch * d.ngroups * N * E);
+    const Range rD = rng(D, D ? (size_t)d.nheads * 4 : 0);
+    for (Range r : {rs, rx, rdt, rA, rB, rC, rD})
+        if (overlap(ry, r)) return SSD_ERR_ALIAS;
+    for (Range r : {rx, rdt, rA, rB, rC, rD})
+        if (overlap(rs, r)) return SSD_ERR_ALIAS;
+    ssd::DecodeParams p{};
+    p.state = state;
+    p.x = x;
+    p.dt = dt;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.y = y;
+    p.H = d.nheads;
+    p.G = d.ngroups;
+    p.P = d.headdim;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool ok = (io == SSD_BF16) ? ssd::decode_launch<ssd::bf16>(N, p, (unsigned)units, s)
+                                     : ssd::decode_launch<float>(N, p, (unsigned)units, s);
+    if (!ok) return SSD_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// ssd_device.h -- device helpers shared by the SSD kernels (gfx950 / CDNA4).
+//
+// MFMA fragments.  All contractions use the 16x16 output tile of the gfx950
+// matrix cores with a K step of 32:
+//   bf16 io: one v_mfma_f32_16x16x32_bf16 per K step;
+//   fp32 io: eight v_mfma_f32_16x16x4_f32 per K step (one per fragment slot).
+// A fragment is 8 values per lane.  Lane l has group g = l / 16 and index
+// i = l % 16.  For the A operand (rows x K) lane l holds row i; for the B
+// operand (K x cols) it holds column i.  Slot e (0..7) of group g carries
+// the K index kmap(g, e); any kmap works as long as A and B use the same one,
+// because the product sums over every (g, e) pair.  The accumulator holds
+// D[4g + r][i] in element r (r = 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Io;
+
+template <> struct Io<bf16> {
+    typedef bf16x8 Frag;
+    typedef bf16x4 Half;
+    static __device__ __forceinline__ f32x4 mfma(f32x4 acc, Frag a, Frag b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+
+template <> struct Io<float> {
+    typedef f32x8 Frag;
+    typedef f32x4 Half;
+    static __device__ __forceinline__ f32x4 mfma(f32x4 acc, Frag a, Frag b) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+template <typename Frag> __device__ __forceinline__ Frag zero_frag() {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 0;
+    return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Transposing LDS read of 16-bit data (gfx950 ds_read_b64_tr_b16): inside a
+// 16-lane group, lane i receives column i%16 of the four rows addressed by
+// lanes 4e..4e+3, where lane 4e+c points at columns [4c, 4c+4) of row e.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16 *p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+}  // namespace ssd

@@ -1,0 +1,138 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/ssd.h declares, and rejects invalid calls synchronously (every case
+here fails validation before anything could be launched)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from selective_state_space_71_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        from selective_state_space_71_amd import build
+        build.build(verbose=False)
+    return ssd.load_library()
+
+
+def test_header_symbols_are_exported(lib):
+    names = ssd.header_functions()
+    assert {"ssd_chunk_scan_fwd", "ssd_decode_step", "ssd_chunk_scan_fwd_workspace_size",
+            "ssd_status_string", "ssd_abi_version", "ssd_chunk_scan_fwd_check"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.ssd_abi_version() == 1
+    for code, name in ssd._STATUS.items():
+        assert lib.ssd_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.ssd_status_string(77)
+
+
+def _dims(**kw):
+    d = dict(batch=2, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=1, nseq=2)
+    d.update(kw)
+    return ssd.SsdDims(*[d[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
+                                         "ngroups", "nseq")])
+
+
+FAKE = 1 << 40   # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, dims, io=ssd.SSD_BF16, Q=256, **ptrs):
+    dp = dict(x=FAKE, dt=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+              C=FAKE + (4 << 30), D=None, init=None, cu=None, y=FAKE + (8 << 30), fin=None,
+              ws=FAKE + (16 << 30), wsb=1 << 40)
+    dp.update(ptrs)
+    return lib.ssd_chunk_scan_fwd(
+        ctypes.byref(dims) if dims is not None else None, io, Q, dp["x"], dp["dt"], dp["A"],
+        dp["B"], dp["C"], dp["D"], dp["init"], dp["cu"], dp["y"], dp["fin"], dp["ws"],
+        ctypes.c_size_t(dp["wsb"]), None)
+
+
+def test_workspace_size_query(lib):
+    n = lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims()), 256, ssd.SSD_BF16)
+    assert n >= 2 * 8 * 64 * 128 * 4            # holds the fp32 boundary states
+    assert n % 256 == 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims()), 100, ssd.SSD_BF16) == 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(None, 256, ssd.SSD_BF16) == 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=48)), 256, ssd.SSD_BF16) == 0
+    # fp32 io with the largest tiles does not fit in LDS
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims()), 256, ssd.SSD_F32) == 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=16, dstate=16)), 64, ssd.SSD_F32) > 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), 1),
+    (dict(io=5), 3),
+    (dict(dims=_dims(seqlen=0)), 2),
+    (dict(dims=_dims(nheads=6, ngroups=4)), 2),
+    (dict(dims=_dims(nseq=3)), 2),                               # dense needs nseq == batch
+    (dict(Q=100), 4),
+    (dict(dims=_dims(headdim=48)), 4),
+    (dict(dims=_dims(dstate=256)), 4),
+    (dict(io=ssd.SSD_F32), 4),                                   # LDS does not fit
+    (dict(x=None), 1),
+    (dict(A=None), 1),
+    (dict(ws=None), 7),
+    (dict(x=FAKE + 2), 5),
+    (dict(ws=FAKE + (16 << 30) + 16), 5),
+    (dict(y=FAKE + 64), 6),                                      # y overlaps x
+    (dict(fin=FAKE + (3 << 30)), 6),                             # final_state overlaps B
+    (dict(wsb=1024), 7),
+])
+def test_forward_validation_rejects(lib, case, expect):
+    dims = case.pop("dims", _dims())
+    assert _fwd(lib, dims, **case) == expect
+
+
+def test_varlen_validation(lib):
+    # cu_seqlens needs batch == 1
+    assert _fwd(lib, _dims(), cu=FAKE + (20 << 30)) == 2
+    # and nseq <= 65536
+    assert _fwd(lib, _dims(batch=1, nseq=70000), cu=FAKE + (20 << 30)) == 2
+
+
+def _dec(lib, dims, io=ssd.SSD_BF16, **ptrs):
+    dp = dict(state=FAKE, x=FAKE + (1 << 34), dt=FAKE + (2 << 34), A=FAKE + (3 << 34),
+              B=FAKE + (4 << 34), C=FAKE + (5 << 34), D=None, y=FAKE + (6 << 34))
+    dp.update(ptrs)
+    return lib.ssd_decode_step(ctypes.byref(dims) if dims is not None else None, io, dp["state"],
+                               dp["x"], dp["dt"], dp["A"], dp["B"], dp["C"], dp["D"], dp["y"], None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), 1),
+    (dict(io=9), 3),
+    (dict(dims=_dims(nheads=0)), 2),
+    (dict(dims=_dims(dstate=48)), 4),
+    (dict(state=None), 1),
+    (dict(y=None), 1),
+    (dict(x=FAKE + (1 << 34) + 8), 5),
+    (dict(y=FAKE + 16), 6),                                      # y overlaps state
+    (dict(x=FAKE + 32), 6),                                      # x overlaps state
+])
+def test_decode_validation_rejects(lib, case, expect):
+    dims = case.pop("dims", _dims())
+    assert _dec(lib, dims, **case) == expect
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.reload(ssd)
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        importlib.reload(ssd)

@@ -1,0 +1,257 @@
+"""GPU parity of the HIP SSD library against the fp64 oracle.
+
+Tolerances (relative L2 over the compared tensor): 1e-4 for fp32 io, 1e-2 for
+bf16 io, with fp32 accumulation and fp32 state.  Because D*x dominates y at
+these value ranges, every forward case is also compared with D = 0 (the
+state-space part alone) and on the final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+from selective_state_space_71_amd import ssd
+from selective_state_space_71_amd import workloads as wl
+from tests import helpers as hp
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(d, chunk_len, D=True, init=True):
+    y, fin = ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"] if D else None,
+                                chunk_len=chunk_len,
+                                init_state=d.get("init_state") if init else None,
+                                cu_seqlens=d.get("cu_seqlens"))
+    assert ssd.check_workspace(ssd.chunk_scan_fwd.last_workspace) == 0
+    return y, fin
+
+
+def _check_fwd(inp, chunk_len, tol=None, tag=""):
+    """Forward with and without D against the oracle; returns the errors."""
+    io = inp["io"]
+    tol = tol or hp.TOL[io]
+    d = hp.to_device(inp, DEV)
+    y_ssm_ref, fin_ref = hp.oracle_fwd(inp, D=False)
+    x64 = wl.as_f64(inp["x"], io)
+    y_ref = y_ssm_ref + inp["D"].astype(np.float64)[None, None, :, None] * x64
+    y, fin = _run(d, chunk_len)
+    y0, fin0 = _run(d, chunk_len, D=False)
+    torch.cuda.synchronize()
+    errs = dict(y=hp.rel_l2(hp.to_numpy64(y), y_ref),
+                y_ssm=hp.rel_l2(hp.to_numpy64(y0), y_ssm_ref),
+                final=hp.rel_l2(hp.to_numpy64(fin), fin_ref),
+                final_noD=hp.rel_l2(hp.to_numpy64(fin0), fin_ref))
+    print(f"[parity] {tag} chunk={chunk_len} io={io} " +
+          " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    assert np.isfinite(hp.to_numpy64(y)).all()
+    return errs
+
+
+# ------------------------------------------------------------------ small cases
+@pytest.mark.parametrize("shape", [
+    # b, L, H, P, N, G, chunk, init
+    (2, 700, 4, 64, 128, 1, 256, True),
+    (1, 300, 4, 64, 128, 2, 64, False),
+    (2, 257, 2, 32, 64, 1, 128, True),
+    (1, 129, 2, 16, 16, 1, 64, True),
+    (1, 1000, 8, 64, 128, 4, 128, True),
+    (3, 64, 2, 64, 32, 1, 64, True),
+    (1, 1, 2, 64, 128, 1, 256, True),
+])
+def test_bf16_small(shape):
+    b, L, H, P, N, G, Q, init = shape
+    inp = wl.make_inputs(b, L, H, P, N, G, io="bf16", seed=hash(shape) % 1000,
+                         init_std=0.5 if init else None)
+    _check_fwd(inp, Q, tag=f"bf16 {shape}")
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 300, 2, 16, 16, 1, 64, True),
+    (2, 200, 2, 32, 32, 1, 128, True),
+    (1, 190, 3, 16, 64, 1, 256, False),
+    (1, 333, 4, 64, 16, 2, 64, True),
+])
+def test_fp32_small(shape):
+    b, L, H, P, N, G, Q, init = shape
+    inp = wl.make_inputs(b, L, H, P, N, G, io="f32", seed=7 + L, init_std=0.5 if init else None)
+    _check_fwd(inp, Q, tag=f"f32 {shape}")
+
+
+def test_workload0_tiny_fp32():
+    _check_fwd(wl.workload_inputs(0), 64, tag="tiny_fp32")
+
+
+def test_chunk_len_invariance_bf16():
+    inp = wl.make_inputs(2, 600, 4, 64, 128, 1, io="bf16", seed=3, init_std=0.3)
+    d = hp.to_device(inp, DEV)
+    ys = [hp.to_numpy64(_run(d, q)[0]) for q in (64, 128, 256)]
+    fins = [hp.to_numpy64(_run(d, q)[1]) for q in (64, 128, 256)]
+    for a in ys[1:]:
+        assert hp.rel_l2(a, ys[0]) <= 1e-2
+    for a in fins[1:]:
+        assert hp.rel_l2(a, fins[0]) <= 1e-2
+    for q in (64, 128, 256):
+        _check_fwd(inp, q, tag="invariance")
+
+
+def test_chunk_len_invariance_fp32():
+    inp = wl.make_inputs(1, 500, 2, 16, 16, 1, io="f32", seed=4, init_std=0.3)
+    for q in (64, 128, 256):
+        _check_fwd(inp, q, tag="invariance f32")
+
+
+# ------------------------------------------------------------------ worked example
+def test_scalar_gate_on_gpu():
+    """Feghi's Mamba review, section 3: 10 and 2 -> 9.2 (g=0.1), 2.8 (g=0.9),
+    as a one-token, partial-chunk fp32 call."""
+    for g, expect in ((0.1, 9.2), (0.9, 2.8)):
+        x = torch.full((1, 1, 1, 16), 2.0, device=DEV)
+        dt = torch.full((1, 1, 1), g, device=DEV)
+        A = torch.tensor([np.log(1 - g) / g], dtype=torch.float32, device=DEV)
+        B = torch.zeros((1, 1, 1, 16), device=DEV)
+        B[..., 0] = 1.0
+        C = B.clone()
+        h0 = torch.zeros((1, 1, 16, 16), device=DEV)
+        h0[0, 0, :, 0] = 10.0
+        y, fin = ssd.chunk_scan_fwd(x, dt, A, B, C, None, chunk_len=64, init_state=h0)
+        torch.cuda.synchronize()
+        assert torch.allclose(y[0, 0, 0], torch.full((16,), expect, device=DEV), atol=1e-5)
+        assert torch.allclose(fin[0, 0, :, 0], torch.full((16,), expect, device=DEV), atol=1e-5)
+
+
+# ------------------------------------------------------------------ boundaries
+def test_varlen_matches_oracle_and_per_sequence_calls():
+    lens = [5, 1, 300, 64, 0, 700, 129]
+    T = sum(lens)
+    inp = wl.make_inputs(1, T, 4, 64, 128, 2, io="bf16", seed=21, init_std=0.4, lengths=lens)
+    for Q in (64, 256):
+        _check_fwd(inp, Q, tag=f"varlen Q={Q}")
+    d = hp.to_device(inp, DEV)
+    y, fin = _run(d, 128)
+    cu = inp["cu_seqlens"]
+    assert torch.equal(fin[4], d["init_state"][4])          # empty sequence keeps its state
+    for s in range(len(lens)):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        if hi == lo:
+            continue
+        ys, fs = ssd.chunk_scan_fwd(d["x"][:, lo:hi].contiguous(), d["dt"][:, lo:hi].contiguous(),
+                                    d["A"], d["B"][:, lo:hi].contiguous(), d["C"][:, lo:hi].contiguous(),
+                                    d["D"], chunk_len=128, init_state=d["init_state"][s:s + 1].contiguous())
+        assert torch.equal(ys, y[:, lo:hi]), s                 # same chunking -> same bits
+        assert torch.equal(fs, fin[s:s + 1]), s
+
+
+def test_varlen_nan_stays_in_its_sequence():
+    lens = [200, 300, 100]
+    inp = wl.make_inputs(1, 600, 2, 64, 128, 1, io="bf16", seed=22, lengths=lens)
+    d = hp.to_device(inp, DEV)
+    x = d["x"].clone()
+    x[0, 250, 1, 3] = float("nan")
+    y, fin = ssd.chunk_scan_fwd(x, d["dt"], d["A"], d["B"], d["C"], d["D"], chunk_len=64,
+                                cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(y[0, :200].float()).all() and torch.isfinite(y[0, 500:].float()).all()
+    assert torch.isfinite(fin[0]).all() and torch.isfinite(fin[2]).all()
+    assert not torch.isfinite(fin[1, 1]).all()
+
+
+def test_split_resume_equals_whole_run():
+    inp = wl.make_inputs(2, 900, 4, 64, 128, 1, io="bf16", seed=23, init_std=0.5)
+    d = hp.to_device(inp, DEV)
+    y, fin = _run(d, 256)
+    k = 333
+    cut = lambda t, lo, hi: t[:, lo:hi].contiguous()
+    y1, f1 = ssd.chunk_scan_fwd(cut(d["x"], 0, k), cut(d["dt"], 0, k), d["A"], cut(d["B"], 0, k),
+                                cut(d["C"], 0, k), d["D"], chunk_len=256, init_state=d["init_state"])
+    y2, f2 = ssd.chunk_scan_fwd(cut(d["x"], k, 900), cut(d["dt"], k, 900), d["A"], cut(d["B"], k, 900),
+                                cut(d["C"], k, 900), d["D"], chunk_len=256, init_state=f1)
+    torch.cuda.synchronize()
+    assert hp.rel_l2(hp.to_numpy64(torch.cat([y1, y2], 1)), hp.to_numpy64(y)) <= 1e-2
+    assert hp.rel_l2(hp.to_numpy64(f2), hp.to_numpy64(fin)) <= 1e-3
+
+
+def test_in_place_state_resume():
+    inp = wl.make_inputs(1, 400, 2, 64, 128, 1, io="bf16", seed=24, init_std=0.5)
+    d = hp.to_device(inp, DEV)
+    ref_y, ref_fin = _run(d, 128)
+    st = d["init_state"].clone()
+    y, fin = ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk_len=128,
+                                init_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    assert torch.equal(y, ref_y) and torch.equal(st, ref_fin)
+
+
+def test_zero_step_keeps_state():
+    inp = wl.make_inputs(1, 300, 2, 64, 128, 1, io="bf16", seed=25, init_std=1.0)
+    inp["dt"][:] = 0.0
+    d = hp.to_device(inp, DEV)
+    y, fin = _run(d, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, d["init_state"])
+    _check_fwd(inp, 128, tag="dt=0")
+
+
+def test_run_to_run_bitwise_deterministic():
+    inp = wl.make_inputs(2, 1500, 8, 64, 128, 1, io="bf16", seed=26, init_std=0.5)
+    d = hp.to_device(inp, DEV)
+    a = _run(d, 256)
+    b = _run(d, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("io,P,N,G", [("bf16", 64, 128, 1), ("f32", 16, 16, 1), ("bf16", 32, 256, 2),
+                                      ("f32", 64, 64, 4), ("bf16", 7, 32, 1)])
+def test_decode_small(io, P, N, G):
+    inp = wl.make_decode_inputs(5, 8, P, N, G, io=io, seed=P + N)
+    d = hp.to_device(inp, DEV)
+    y_ref, st_ref = hp.oracle_decode(inp)
+    st = d["state"].clone()
+    y = ssd.decode_step(st, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    torch.cuda.synchronize()
+    tol = hp.TOL[io]
+    assert hp.rel_l2(hp.to_numpy64(y), y_ref) <= tol
+    assert hp.rel_l2(hp.to_numpy64(st), st_ref) <= 1e-6
+
+
+def test_decode_steps_equal_forward():
+    """T decode steps from h0 == the forward pass over those T tokens."""
+    T = 40
+    inp = wl.make_inputs(2, T, 4, 64, 128, 1, io="f32", seed=27, init_std=0.5)
+    d = hp.to_device(inp, DEV)
+    y_f, fin_f = _run(d, 64)
+    st = d["init_state"].clone()
+    ys = []
+    for t in range(T):
+        ys.append(ssd.decode_step(st, d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
+                                  d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), d["D"]))
+    torch.cuda.synchronize()
+    yd = torch.stack(ys, 1)
+    assert hp.rel_l2(hp.to_numpy64(yd), hp.to_numpy64(y_f)) <= 1e-4
+    assert hp.rel_l2(hp.to_numpy64(st), hp.to_numpy64(fin_f)) <= 1e-4
+
+
+# ------------------------------------------------------------------ full workloads
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_full_workload_forward(index):
+    w = wl.WORKLOADS[index]
+    print(f"[parity] full workload {w['name']}", flush=True)
+    _check_fwd(wl.workload_inputs(index), w["chunk"], tag=w["name"])
+
+
+def test_full_workload_decode():
+    inp = wl.workload_inputs(4)
+    d = hp.to_device(inp, DEV)
+    y_ref, st_ref = hp.oracle_decode(inp)
+    st = d["state"]
+    y = ssd.decode_step(st, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    torch.cuda.synchronize()
+    ey = hp.rel_l2(hp.to_numpy64(y), y_ref)
+    es = hp.rel_l2(hp.to_numpy64(st), st_ref)
+    print(f"[parity] decode y={ey:.3e} state={es:.3e}", flush=True)
+    assert ey <= 1e-2 and es <= 1e-6
