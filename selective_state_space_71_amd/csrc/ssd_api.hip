@@ -6,7 +6,7 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "ssd_device.h"
 #include "ssd_fwd_kernel.h"
 
@@ -369,7 +369,6 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
     fp.H = d.nheads;
     fp.G = d.ngroups;
     const unsigned grid = (unsigned)(w.max_entries * d.nheads);
-    fp.grid = grid;
     hipError_t err = hipSuccess;
     const bool ok = (io == SSD_BF16)
                         ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, fp, grid, s, true, &err)

@@ -5,24 +5,31 @@
 // form, carry chunk-boundary states between chunks, fold them back into the
 // outputs).  Per (sequence, head h, chunk c) with in-chunk index i in [0, q),
 // a_t = dt_t A_h and s_i the inclusive in-chunk cumulative sum of a:
-//   Y_diag = (C B^T o Lambda) diag(dt) X,   Lambda_ij = exp(s_i - s_j), j <= i
-//   S_c    = X^T diag(exp(s_{q-1} - s_j) dt_j) B         (chunk state from 0)
+//   Y_diag  = (C B^T o Lambda) diag(dt) X,   Lambda_ij = exp(s_i - s_j), j <= i
+//   S_c     = X^T diag(exp(s_{q-1} - s_j) dt_j) B        (chunk state from 0)
 //   H_{c+1} = exp(s_{q-1}) H_c + S_c                     (inter-chunk recurrence)
-//   Y_off  = diag(exp(s_i)) C H_c^T
-//   y      = Y_diag + Y_off + D_h x
+//   Y_off   = diag(exp(s_i)) C H_c^T
+//   y       = Y_diag + Y_off + D_h x
 //
-// One workgroup (4 waves) owns one (chunk, head).  Workgroups take a ticket
-// from a global counter; tickets are ordered chunk-index-major, so the
-// workgroup holding chunk c-1 of the same (sequence, head) always started
-// earlier.  Each workgroup computes S_c first, then waits for its
-// predecessor's boundary state (a progress flag per (sequence, head)),
-// publishes H_{c+1} and only then computes the outputs, so the serial chain
-// carries just a P x N fp32 state per link.  The state buffer is the caller's
-// final_state (or workspace): after the last chunk it holds the final state.
+// Scheduling.  One workgroup (8 waves) owns one (chunk, head).  Workgroups
+// take a ticket from a global counter; tickets are ordered chunk-index-major,
+// so the workgroup holding chunk c-1 of the same (sequence, head) always
+// started earlier and the chain cannot deadlock.  Each workgroup forms S_c
+// first, then waits for its predecessor's boundary state (a progress flag per
+// (sequence, head)), publishes H_{c+1}, and only then computes the outputs:
+// the serial chain carries one P x N fp32 state per link.  The state buffer is
+// the caller's final_state (or workspace) and ends up holding the final state.
 //
-// LDS (per workgroup): B chunk [Q][N] (row layout), x^T scaled by dt and by
-// the chunk-end decay (two [P][Q] copies; the second is reused for the
-// incoming state as io), and per-token s, dt, exp(s).
+// Numerics.  All decays are products of factors <= 1 (A <= 0, dt >= 0):
+// for a 16 x 16 tile (I, J) below the diagonal,
+//   exp(s_i - s_j) = exp(s_i - s_r) * exp(s_r - s_j),  r = last token of tile J,
+// so only the diagonal tiles need a per-element exponential; the chunk-state
+// weights exp(s_{q-1} - s_j) and the read-out weights exp(s_i) are per-token
+// vectors.  Exponentials are evaluated as exp2 of log2(e)-scaled sums.
+//
+// LDS: the B chunk [Q][N] (row layout; transposed fragments come from the
+// gfx950 transposing LDS read), the raw x chunk transposed [P][Q], the
+// incoming state as io [P][N], and per-token vectors.
 #pragma once
 
 #include "ssd_device.h"
@@ -45,60 +52,99 @@ struct FwdParams {
     int *flags;               // per (sequence, head): chunks whose state is published
     int *error;
     int H, G;
-    long long grid;           // workgroups launched
 };
 
-template <int v> struct IntC { static constexpr int value = v; };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 template <typename IO, int P, int N, int Q>
 struct FwdShape {
-    static constexpr int kThreads = 256;
-    static constexpr int kWaves = 4;
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
     static constexpr int PT = P / 16;            // 16-wide tiles over the head dim
     static constexpr int NT = N / 16;            // 16-wide tiles over the state dim
     static constexpr int NK = (N + 31) / 32;     // K steps over the state dim
     static constexpr int NP = NK * 32;           // state dim padded to a K step
     static constexpr int QT = Q / 16;            // 16-row tiles of a chunk
     static constexpr int QK = Q / 32;            // K steps over a chunk
-    static constexpr int NTW = (NT + kWaves - 1) / kWaves;  // state tiles per wave
+    // chunk-state work split: WN waves along the state dim, WP along the head dim
+    static constexpr int WN = cmin(NT, kWaves);
+    static constexpr int WP = kWaves / WN;
+    static constexpr int NTW = (NT + WN - 1) / WN;   // state tiles per wave
+    static constexpr int PTW = (PT + WP - 1) / WP;   // head-dim tiles per wave
     static constexpr int E = (int)sizeof(IO);
     static constexpr int PAD = 16 / E;           // 16 bytes of padding per LDS row
     static constexpr int SB = NP + PAD;          // row stride of the B tile
-    static constexpr int SX = Q + PAD;           // row stride of the x^T tiles
+    static constexpr int SX = Q + PAD;           // row stride of the x^T tile
     static constexpr int SH = NP + PAD;          // row stride of the incoming state
     static constexpr int kLdsB = Q * SB * E;
-    static constexpr int kLdsXd = P * SX * E;
-    static constexpr int kLdsXw = cmax(P * SX, P * SH) * E;
-    static constexpr int kLdsScal = 3 * Q * 4;
-    static constexpr int kLds = kLdsB + kLdsXd + kLdsXw + kLdsScal + 16;
+    static constexpr int kLdsX = P * SX * E;
+    static constexpr int kLdsH = P * SH * E;
+    static constexpr int kNVec = 6;              // per-token float vectors
+    static constexpr int kLdsVec = kNVec * Q * 4;
+    static constexpr int kLds = kLdsB + kLdsX + kLdsH + kLdsVec + 16;
     static constexpr bool kFits = kLds <= 160 * 1024;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2f_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
 // Row tile handled by `wave` in its round `k`: a snake order over the waves,
 // so that every wave gets a similar share of the causal (triangular) work.
 __device__ __forceinline__ int snake_tile(int wave, int k, int nwaves) {
-    const int blk = k;
-    return blk * nwaves + ((blk & 1) ? (nwaves - 1 - wave) : wave);
+    return k * nwaves + ((k & 1) ? (nwaves - 1 - wave) : wave);
+}
+
+// Unscaled B^T fragment: lane holds B[k0 + 8*lg + e][n0 + li], e = 0..7.
+template <typename IO, int SB>
+__device__ __forceinline__ typename Io<IO>::Frag load_bt_frag(const IO *sB, int k0, int n0, int li, int lg) {
+    typename Io<IO>::Frag f;
+    if constexpr (sizeof(IO) == 2) {
+        const int row = k0 + 8 * lg + (li >> 2);
+        const int col = n0 + 4 * (li & 3);
+        const bf16x4 lo = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + row * SB + col));
+        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + (row + 4) * SB + col));
+        f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = sB[(k0 + 8 * lg + e) * SB + n0 + li];
+    }
+    return f;
+}
+
+// Slot-wise scaling of a fragment: slot e by lo[e] (e < 4) or hi[e - 4].
+template <typename IO>
+__device__ __forceinline__ typename Io<IO>::Frag scale_frag(typename Io<IO>::Frag f, f32x4 lo, f32x4 hi) {
+    typename Io<IO>::Frag o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[e] = from_f32<IO>(to_f32(f[e]) * lo[e]);
+        o[e + 4] = from_f32<IO>(to_f32(f[e + 4]) * hi[e]);
+    }
+    return o;
 }
 
 template <typename IO, int P, int N, int Q>
-__global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
+__global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     typedef FwdShape<IO, P, N, Q> S;
     typedef typename Io<IO>::Frag Frag;
+    typedef typename Io<IO>::Half Half;
     static_assert(S::kFits, "chunk tiles do not fit in LDS");
 
     __shared__ __attribute__((aligned(16))) char smem[S::kLds];
     IO *sB = reinterpret_cast<IO *>(smem);
-    IO *sXd = reinterpret_cast<IO *>(smem + S::kLdsB);
-    IO *sXw = reinterpret_cast<IO *>(smem + S::kLdsB + S::kLdsXd);
-    IO *sH = sXw;  // reused once the chunk state is formed
-    float *sS = reinterpret_cast<float *>(smem + S::kLdsB + S::kLdsXd + S::kLdsXw);
-    float *sDt = sS + Q;
-    float *sE = sDt + Q;
-    int *sTicket = reinterpret_cast<int *>(sE + Q);
+    IO *sX = reinterpret_cast<IO *>(smem + S::kLdsB);
+    IO *sH = reinterpret_cast<IO *>(smem + S::kLdsB + S::kLdsX);
+    float *vS2 = reinterpret_cast<float *>(smem + S::kLdsB + S::kLdsX + S::kLdsH);  // s * log2(e)
+    float *vDt = vS2 + Q;     // dt_j
+    float *vCol = vDt + Q;    // exp(s_r - s_j) dt_j, r = last token of j's 16-tile
+    float *vW = vCol + Q;     // exp(s_last - s_j) dt_j
+    float *vEo = vW + Q;      // exp(s_i)
+    float *vRef = vEo + Q;    // s2 of the last token of each 16-tile (QT used)
+    int *sTicket = reinterpret_cast<int *>(vRef + Q);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -122,15 +168,47 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
     const int g = h / (H / G);
     const float Ah = prm.A[h];
     const float Dh = prm.D ? prm.D[h] : 0.f;
-    const long long xs = (long long)H * P;   // token stride of x and y
-    const long long bs = (long long)G * N;   // token stride of B and C
-    const IO *xg = reinterpret_cast<const IO *>(prm.x) + tok0 * xs + (long long)h * P;
-    const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + (long long)g * N;
-    const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + (long long)g * N;
-    IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + (long long)h * P;
+    const int xs = H * P;    // token stride of x and y (elements)
+    const int bs = G * N;    // token stride of B and C
+    const IO *xg = reinterpret_cast<const IO *>(prm.x) + tok0 * xs + h * P;
+    const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + g * N;
+    const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + g * N;
+    IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
     const float *dtg = prm.dt + tok0 * H + h;
 
-    // ---- in-chunk cumulative sum of dt*A (wave 0, one wave-wide scan) ----
+    // ---- issue the global loads of the B and x chunks early ----
+    constexpr int VPR = S::NP * S::E / 16;          // 16-byte vectors per B row in LDS
+    constexpr int VN = N * S::E / 16;               // vectors that hold data
+    constexpr int NVB = (Q * VPR + S::kThreads - 1) / S::kThreads;
+    i32x4 bval[NVB];
+#pragma unroll
+    for (int k = 0; k < NVB; ++k) {
+        const int v = tid + k * S::kThreads;
+        const int j = v / VPR;
+        const int c = v - j * VPR;
+        bval[k] = i32x4{0, 0, 0, 0};
+        if (v < Q * VPR && j < q && c < VN)
+            bval[k] = *reinterpret_cast<const i32x4 *>(Bg + j * bs + c * (16 / S::E));
+    }
+    // x: a unit is 4 consecutive tokens x 8 channels
+    constexpr int PB = P / 8;
+    constexpr int NUNIT = (Q / 4) * PB;
+    constexpr int NU = (NUNIT + S::kThreads - 1) / S::kThreads;
+    Frag xr[NU][4];
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+        const int u = tid + k * S::kThreads;
+        const int it = u / PB;
+        const int p0 = (u - it * PB) * 8;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = 4 * it + t;
+            xr[k][t] = zero_frag<Frag>();
+            if (u < NUNIT && i < q) xr[k][t] = *reinterpret_cast<const Frag *>(xg + i * xs + p0);
+        }
+    }
+
+    // ---- in-chunk cumulative sum of dt*A (wave 0) and per-token vectors ----
     if (wave == 0) {
         constexpr int R = Q / 64;
         float a[R];
@@ -139,7 +217,7 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
         for (int k = 0; k < R; ++k) {
             const int i = lane * R + k;
             const float d = (i < q) ? dtg[(long long)i * H] : 0.f;
-            sDt[i] = d;
+            vDt[i] = d;
             run += d * Ah;
             a[k] = run;
         }
@@ -151,100 +229,101 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
         }
         const float excl = incl - run;
 #pragma unroll
-        for (int k = 0; k < R; ++k) sS[lane * R + k] = excl + a[k];
+        for (int k = 0; k < R; ++k) vS2[lane * R + k] = (excl + a[k]) * kLog2e;
     }
-    __syncthreads();
-    const float s_last = sS[Q - 1];
-    for (int i = tid; i < Q; i += S::kThreads) sE[i] = __expf(sS[i]);
-
-    // ---- stage the B chunk, row layout [j][n], zero outside the chunk ----
-    {
-        constexpr int VPR = S::NP * S::E / 16;  // 16-byte vectors per LDS row
-        constexpr int VN = N * S::E / 16;       // vectors that hold data
-        for (int v = tid; v < Q * VPR; v += S::kThreads) {
-            const int j = v / VPR;
-            const int c = v - j * VPR;
-            i32x4 val = {0, 0, 0, 0};
-            if (j < q && c < VN)
-                val = *reinterpret_cast<const i32x4 *>(Bg + (long long)j * bs + c * (16 / S::E));
-            *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = val;
-        }
+    // stage B rows while wave 0 scans
+#pragma unroll
+    for (int k = 0; k < NVB; ++k) {
+        const int v = tid + k * S::kThreads;
+        const int j = v / VPR;
+        const int c = v - j * VPR;
+        if (v < Q * VPR) *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = bval[k];
     }
-    // ---- stage x^T scaled by dt (sXd) and by the chunk-end decay (sXw) ----
-    {
-        constexpr int PB = P / 8;
-        for (int u = tid; u < (Q / 2) * PB; u += S::kThreads) {
-            const int ip = u / PB;
-            const int p0 = (u - ip * PB) * 8;
-            const int i0 = 2 * ip;
-            float v0[8], v1[8];
+    // stage x transposed: x^T[p][i .. i+3] from 4 tokens of one channel
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { v0[e] = 0.f; v1[e] = 0.f; }
-            if (i0 < q) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v0[e] = to_f32(xg[(long long)i0 * xs + p0 + e]);
-            }
-            if (i0 + 1 < q) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v1[e] = to_f32(xg[(long long)(i0 + 1) * xs + p0 + e]);
-            }
-            const float d0 = sDt[i0], d1 = sDt[i0 + 1];
-            const float w0 = __expf(s_last - sS[i0]) * d0;
-            const float w1 = __expf(s_last - sS[i0 + 1]) * d1;
+    for (int k = 0; k < NU; ++k) {
+        const int u = tid + k * S::kThreads;
+        if (u < NUNIT) {
+            const int it = u / PB;
+            const int p0 = (u - it * PB) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                IO *pd = sXd + (p0 + e) * S::SX + i0;
-                IO *pw = sXw + (p0 + e) * S::SX + i0;
-                pd[0] = from_f32<IO>(v0[e] * d0);
-                pd[1] = from_f32<IO>(v1[e] * d1);
-                pw[0] = from_f32<IO>(v0[e] * w0);
-                pw[1] = from_f32<IO>(v1[e] * w1);
+                Half v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = xr[k][t][e];
+                *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + 4 * it) = v;
             }
         }
     }
     __syncthreads();
+    const float s2_last = vS2[Q - 1];
+    for (int i = tid; i < Q; i += S::kThreads) {
+        const float s2 = vS2[i];
+        const float d = vDt[i];
+        const float ref = vS2[i | 15];
+        vCol[i] = exp2f_fast(ref - s2) * d;
+        vW[i] = exp2f_fast(s2_last - s2) * d;
+        vEo[i] = exp2f_fast(s2);
+        if ((i & 15) == 15) vRef[i >> 4] = s2;
+    }
+    if constexpr (S::NP != N) {
+        for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
+            const int p = v / (S::NP - N);
+            sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
+        }
+    }
+    __syncthreads();
 
-    // ---- chunk state S_c = (x w)^T B : P x N, K = chunk tokens ----
-    f32x4 accS[S::NTW][S::PT];
+    // ---- chunk state, transposed: S_c^T = (B^T o w) x : N x P, K = chunk ----
+    // Accumulator element r of tile (nt, pt) is S_c[p][n] with
+    // p = pt*16 + li and n = nt*16 + 4*lg + r (four consecutive state columns).
+    const int wn = wave % S::WN;
+    const int wp = wave / S::WN;
+    f32x4 accS[S::NTW][S::PTW];
 #pragma unroll
     for (int a = 0; a < S::NTW; ++a)
 #pragma unroll
-        for (int b = 0; b < S::PT; ++b) accS[a][b] = zero4();
-#pragma unroll 1
-    for (int ks = 0; ks < S::QK; ++ks) {
-        Frag af[S::PT];
+        for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
+    if (wp < S::PT) {
+#pragma unroll 2
+        for (int ks = 0; ks < S::QK; ++ks) {
+            const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg);
+            const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg + 4);
+            Frag xf[S::PTW];
 #pragma unroll
-        for (int pt = 0; pt < S::PT; ++pt)
-            af[pt] = *reinterpret_cast<const Frag *>(sXw + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+            for (int b = 0; b < S::PTW; ++b) {
+                const int pt = wp + b * S::WP;
+                xf[b] = zero_frag<Frag>();
+                if (pt < S::PT)
+                    xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+            }
 #pragma unroll
-        for (int a = 0; a < S::NTW; ++a) {
-            const int nt = wave + a * S::kWaves;
-            if (nt < S::NT) {
-                Frag bfr;
-                if constexpr (sizeof(IO) == 2) {
-                    const int row = ks * 32 + 8 * lg + (li >> 2);
-                    const int col = nt * 16 + 4 * (li & 3);
-                    const bf16x4 lo = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + row * S::SB + col));
-                    const bf16x4 hi = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + (row + 4) * S::SB + col));
-                    bfr = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                } else {
+            for (int a = 0; a < S::NTW; ++a) {
+                const int nt = wn + a * S::WN;
+                if (nt < S::NT) {
+                    const Frag bt = scale_frag<IO>(load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg), wlo, whi);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bfr[e] = sB[(ks * 32 + 8 * lg + e) * S::SB + nt * 16 + li];
+                    for (int b = 0; b < S::PTW; ++b) {
+                        const int pt = wp + b * S::WP;
+                        if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, xf[b]);
+                    }
                 }
-#pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt) accS[a][pt] = Io<IO>::mfma(accS[a][pt], af[pt], bfr);
             }
         }
     }
-    __syncthreads();  // sXw is about to be overwritten with the incoming state
 
     // ---- wait for the incoming boundary state, publish the outgoing one ----
+    // The boundary state and the progress flag are accessed with device-scope
+    // coherent operations (sc1): stores write through to the device coherence
+    // point and loads read from it, so no L2 write-back or invalidate is
+    // needed.  The producer waits until its state stores are acknowledged
+    // before the flag store; the consumer polls the flag and only then loads.
     const int unit = seq * H + h;
     if (cloc > 0) {
         if (tid == 0) {
             int it = 0;
-            while (__hip_atomic_load(prm.flags + unit, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < cloc) {
-                __builtin_amdgcn_s_sleep(2);
+            while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < cloc) {
+                __builtin_amdgcn_s_sleep(1);
                 if (++it > (1 << 22)) {
                     atomicOr(prm.error, 1);
                     break;
@@ -252,38 +331,51 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
             }
         }
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     const float *hin = (cloc == 0) ? (prm.init_state ? prm.init_state + (long long)unit * P * N : nullptr)
                                    : prm.state + (long long)unit * P * N;
     float *hout = prm.state + (long long)unit * P * N;
-    const float alpha = __expf(s_last);
-    if constexpr (S::NP != N) {
-        for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
-            const int p = v / (S::NP - N);
-            sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
-        }
-    }
+    const float alpha = exp2f_fast(s2_last);
+    if (wp < S::PT) {
+        constexpr int kDevice = 16;  // cache policy: sc1 (device scope)
+        const __amdgpu_buffer_rsrc_t rin =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(hin), 0, hin ? P * N * 4 : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
+        f32x4 hv[S::NTW][S::PTW];
 #pragma unroll
-    for (int a = 0; a < S::NTW; ++a) {
-        const int nt = wave + a * S::kWaves;
-        if (nt < S::NT) {
+        for (int a = 0; a < S::NTW; ++a)
 #pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt)
+            for (int b = 0; b < S::PTW; ++b) {
+                const int nt = wn + a * S::WN, pt = wp + b * S::WP;
+                hv[a][b] = zero4();
+                if (nt < S::NT && pt < S::PT && hin)
+                    hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kDevice));
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = pt * 16 + 4 * lg + r;
-                    const int n = nt * 16 + li;
-                    const float hv = hin ? hin[p * N + n] : 0.f;
-                    hout[p * N + n] = alpha * hv + accS[a][pt][r];
-                    sH[p * S::SH + n] = from_f32<IO>(hv);
+        for (int a = 0; a < S::NTW; ++a)
+#pragma unroll
+            for (int b = 0; b < S::PTW; ++b) {
+                const int nt = wn + a * S::WN, pt = wp + b * S::WP;
+                if (nt < S::NT && pt < S::PT) {
+                    const int p = pt * 16 + li;
+                    const int n0 = nt * 16 + 4 * lg;
+                    f32x4 o;
+                    Half hb;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        o[r] = alpha * hv[a][b][r] + accS[a][b][r];
+                        hb[r] = from_f32<IO>(hv[a][b][r]);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout, (p * N + n0) * 4, 0,
+                                                           kDevice);
+                    *reinterpret_cast<Half *>(sH + p * S::SH + n0) = hb;
                 }
-        }
+            }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
     __syncthreads();
-    if (tid == 0)
-        __hip_atomic_store(prm.flags + unit, cloc + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(prm.flags + unit, cloc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- outputs, one 16-row tile at a time ----
 #pragma unroll 1
@@ -292,17 +384,15 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
         if (I >= S::QT) break;
         const int i0 = I * 16;
         if (i0 >= q) continue;
-        // C rows as fragments (B operand of C B^T, A operand of C H^T)
+        // C rows as fragments (B operand of B C^T, A operand of C H^T)
         Frag cf[S::NK];
         {
             const int i = i0 + li;
 #pragma unroll
             for (int ks = 0; ks < S::NK; ++ks) {
                 const int n0 = ks * 32 + 8 * lg;
-                if (i < q && n0 < N)
-                    cf[ks] = *reinterpret_cast<const Frag *>(Cg + (long long)i * bs + n0);
-                else
-                    cf[ks] = zero_frag<Frag>();
+                cf[ks] = zero_frag<Frag>();
+                if (i < q && n0 < N) cf[ks] = *reinterpret_cast<const Frag *>(Cg + i * bs + n0);
             }
         }
         f32x4 accO[S::PT], accY[S::PT];
@@ -316,9 +406,9 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
                 const Frag hf = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
                 accO[pt] = Io<IO>::mfma(accO[pt], cf[ks], hf);
             }
-        // diagonal block: (C B^T o Lambda) (dt x)
-        const float s_i = sS[i0 + li];
+        // diagonal block: (C B^T o Lambda) diag(dt) x, 32 columns per step
         const int i_row = i0 + li;
+        const float s2_i = vS2[i_row];
 #pragma unroll 1
         for (int kj = 0; kj <= I / 2; ++kj) {
             f32x4 gt[2];
@@ -334,37 +424,53 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(FwdParams prm) {
                     }
                 }
             }
+            // lane holds G[i_row][j] for j = 32 kj + 16 half + 4 lg + r
             Frag m;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int half = e >> 2;
-                const int j = 32 * kj + 16 * half + 4 * lg + (e & 3);
-                const float v = (j <= i_row) ? gt[half][e & 3] * __expf(s_i - sS[j]) : 0.f;
-                m[e] = from_f32<IO>(v);
+            for (int half = 0; half < 2; ++half) {
+                const int jt = 2 * kj + half;
+                const int j0 = 32 * kj + 16 * half + 4 * lg;
+                if (jt < I) {
+                    const float rowf = exp2f_fast(s2_i - vRef[jt]);
+                    const f32x4 col = *reinterpret_cast<const f32x4 *>(vCol + j0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gt[half][r] * rowf * col[r]);
+                } else if (jt == I) {
+                    const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
+                    const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = gt[half][r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
+                        m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(0.f);
+                }
             }
 #pragma unroll
             for (int pt = 0; pt < S::PT; ++pt) {
-                const IO *xr = sXd + (pt * 16 + li) * S::SX + 32 * kj + 4 * lg;
-                typedef typename Io<IO>::Half Half;
-                const Half lo = *reinterpret_cast<const Half *>(xr);
-                const Half hi = *reinterpret_cast<const Half *>(xr + 16);
+                const IO *xrp = sX + (pt * 16 + li) * S::SX + 32 * kj + 4 * lg;
+                const Half lo = *reinterpret_cast<const Half *>(xrp);
+                const Half hi = *reinterpret_cast<const Half *>(xrp + 16);
                 const Frag xf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 accY[pt] = Io<IO>::mfma(accY[pt], m, xf);
             }
         }
-        // y = Y_diag + exp(s_i) Y_off + D x
+        // y = Y_diag + exp(s_i) Y_off + D x, rows i0 + 4 lg + r
+        const f32x4 eo = *reinterpret_cast<const f32x4 *>(vEo + i0 + 4 * lg);
 #pragma unroll
-        for (int pt = 0; pt < S::PT; ++pt)
+        for (int pt = 0; pt < S::PT; ++pt) {
+            const Half xv = *reinterpret_cast<const Half *>(sX + (pt * 16 + li) * S::SX + i0 + 4 * lg);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = i0 + 4 * lg + r;
                 if (i < q) {
-                    const int p = pt * 16 + li;
-                    const float xv = to_f32(xg[(long long)i * xs + p]);
-                    const float yv = accY[pt][r] + sE[i] * accO[pt][r] + Dh * xv;
-                    yg[(long long)i * xs + p] = from_f32<IO>(yv);
+                    const float yv = accY[pt][r] + eo[r] * accO[pt][r] + Dh * to_f32(xv[r]);
+                    yg[i * xs + pt * 16 + li] = from_f32<IO>(yv);
                 }
             }
+        }
     }
 }
 

@@ -12,7 +12,7 @@ static bool fwd_try(int p, int n, int qq, const FwdParams &prm, unsigned grid, h
     if (p != P || n != N || qq != Q) return false;
     if constexpr (FwdShape<IO, P, N, Q>::kFits) {
         if (launch) {
-            hipLaunchKernelGGL((ssd_fwd_kernel<IO, P, N, Q>), dim3(grid), dim3(256), 0, st, prm);
+            hipLaunchKernelGGL((ssd_fwd_kernel<IO, P, N, Q>), dim3(grid), dim3(FwdShape<IO, P, N, Q>::kThreads), 0, st, prm);
             *err = hipGetLastError();
         }
         return true;
