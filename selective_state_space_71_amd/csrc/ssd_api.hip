@@ -11,9 +11,9 @@
 #include "ssd_fwd_kernel.h"
 
 namespace ssd {
-bool fwd_dispatch_bf16(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
+bool fwd_dispatch_bf16(int p, int n, int q, const FwdParams &prm, long long max_entries, hipStream_t st,
                        bool launch, hipError_t *err);
-bool fwd_dispatch_f32(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
+bool fwd_dispatch_f32(int p, int n, int q, const FwdParams &prm, long long max_entries, hipStream_t st,
                       bool launch, hipError_t *err);
 
 // ---------------------------------------------------------------------------
@@ -205,6 +205,18 @@ bool overlap(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
+// Compute units of the current device (cached per device id).
+int num_compute_units() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    return n;
+}
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -368,11 +380,19 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
     fp.error = pp.error;
     fp.H = d.nheads;
     fp.G = d.ngroups;
-    const unsigned grid = (unsigned)(w.max_entries * d.nheads);
+    // head slice per workgroup: about two workgroups per compute unit
+    const int cus = num_compute_units();
+    if (cus <= 0) return SSD_ERR_HIP;
+    const int hpg = d.nheads / d.ngroups;
+    const long long want = 2LL * cus;
+    long long hs = (w.max_entries * d.nheads + want - 1) / want;
+    hs = hs < 1 ? 1 : (hs > hpg ? hpg : hs);
+    fp.heads_per_item = (int)hs;
+    fp.slices = (int)((hpg + hs - 1) / hs);
     hipError_t err = hipSuccess;
     const bool ok = (io == SSD_BF16)
-                        ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, fp, grid, s, true, &err)
-                        : ssd::fwd_dispatch_f32(d.headdim, d.dstate, chunk_len, fp, grid, s, true, &err);
+                        ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, fp, w.max_entries, s, true, &err)
+                        : ssd::fwd_dispatch_f32(d.headdim, d.dstate, chunk_len, fp, w.max_entries, s, true, &err);
     if (!ok) return SSD_ERR_UNSUPPORTED;
     if (err != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;

@@ -2,8 +2,5 @@
 #include "ssd_fwd_launch.h"
 
 namespace ssd {
-bool fwd_dispatch_f32(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
-                      bool launch, hipError_t *err) {
-    return fwd_dispatch<float>(p, n, q, prm, grid, st, launch, err);
-}
+bool fwd_dispatch_f32(SSD_FWD_PARAMS) { return fwd_dispatch<float>(SSD_FWD_ARGS); }
 }  // namespace ssd

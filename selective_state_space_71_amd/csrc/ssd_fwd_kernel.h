@@ -5,20 +5,31 @@
 // form, carry chunk-boundary states between chunks, fold them back into the
 // outputs).  Per (sequence, head h, chunk c) with in-chunk index i in [0, q),
 // a_t = dt_t A_h and s_i the inclusive in-chunk cumulative sum of a:
-//   Y_diag  = (C B^T o Lambda) diag(dt) X,   Lambda_ij = exp(s_i - s_j), j <= i
+//   G       = C B^T                                      (per chunk and group)
+//   Y_diag  = (G o Lambda) diag(dt) X,   Lambda_ij = exp(s_i - s_j), j <= i
 //   S_c     = X^T diag(exp(s_{q-1} - s_j) dt_j) B        (chunk state from 0)
 //   H_{c+1} = exp(s_{q-1}) H_c + S_c                     (inter-chunk recurrence)
 //   Y_off   = diag(exp(s_i)) C H_c^T
 //   y       = Y_diag + Y_off + D_h x
 //
-// Scheduling.  One workgroup (8 waves) owns one (chunk, head).  Workgroups
-// take a ticket from a global counter; tickets are ordered chunk-index-major,
-// so the workgroup holding chunk c-1 of the same (sequence, head) always
-// started earlier and the chain cannot deadlock.  Each workgroup forms S_c
-// first, then waits for its predecessor's boundary state (a progress flag per
-// (sequence, head)), publishes H_{c+1}, and only then computes the outputs:
-// the serial chain carries one P x N fp32 state per link.  The state buffer is
-// the caller's final_state (or workspace) and ends up holding the final state.
+// Work decomposition.  A workgroup (8 waves) owns one chunk of one B/C group
+// and a slice of that group's heads.  C B^T depends only on the chunk and the
+// group (heads of a group share B and C: the multi-input head pattern of
+// section 3-2(5)), so it is formed once per workgroup and kept in registers:
+// wave w owns the 16-row tiles w and 15 - w of the chunk (balanced causal
+// work) and holds their lower-triangular C B^T tiles.  B stays in LDS and the
+// wave's C rows stay in registers while the workgroup walks over its heads;
+// per head only x and dt are loaded (prefetched during the previous head).
+//
+// Chain.  Workgroups take tickets from a global counter; tickets follow the
+// chunk schedule, which is chunk-index-major, so the workgroup holding chunk
+// c-1 of the same (sequence, head slice) always started earlier and walks the
+// heads in the same order: the chain cannot deadlock.  For each head the
+// workgroup forms S_c first, then waits for the predecessor's boundary state
+// (a progress flag per (sequence, head)), computes the diagonal block of its
+// first tile while the state loads are in flight, publishes H_{c+1}, and
+// finishes the outputs.  The state buffer is the caller's final_state (or
+// workspace); it ends up holding the final state.
 //
 // Numerics.  All decays are products of factors <= 1 (A <= 0, dt >= 0):
 // for a 16 x 16 tile (I, J) below the diagonal,
@@ -26,11 +37,10 @@
 // so only the diagonal tiles need a per-element exponential; the chunk-state
 // weights exp(s_{q-1} - s_j) and the read-out weights exp(s_i) are per-token
 // vectors.  Exponentials are evaluated as exp2 of log2(e)-scaled sums.
-//
-// LDS: the B chunk [Q][N] (row layout; transposed fragments come from the
-// gfx950 transposing LDS read), the raw x chunk transposed [P][Q], the
-// incoming state as io [P][N], and per-token vectors.
+// Accumulation and the boundary state are fp32.
 #pragma once
+
+#include <type_traits>
 
 #include "ssd_device.h"
 
@@ -52,6 +62,8 @@ struct FwdParams {
     int *flags;               // per (sequence, head): chunks whose state is published
     int *error;
     int H, G;
+    int heads_per_item;       // head slice length (the last slice of a group may be shorter)
+    int slices;               // slices per group: ceil((H / G) / heads_per_item)
 };
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -65,8 +77,10 @@ struct FwdShape {
     static constexpr int NT = N / 16;            // 16-wide tiles over the state dim
     static constexpr int NK = (N + 31) / 32;     // K steps over the state dim
     static constexpr int NP = NK * 32;           // state dim padded to a K step
-    static constexpr int QT = Q / 16;            // 16-row tiles of a chunk
+    static constexpr int QT = Q / 16;            // 16-row tiles of a chunk (<= 2 per wave)
     static constexpr int QK = Q / 32;            // K steps over a chunk
+    static constexpr bool kTwoTiles = QT > kWaves;   // waves own tiles w and 2*kWaves-1-w
+    static constexpr int GT = kTwoTiles ? QT + 1 : QT; // C B^T tiles held per wave
     // chunk-state work split: WN waves along the state dim, WP along the head dim
     static constexpr int WN = cmin(NT, kWaves);
     static constexpr int WP = kWaves / WN;
@@ -74,7 +88,7 @@ struct FwdShape {
     static constexpr int PTW = (PT + WP - 1) / WP;   // head-dim tiles per wave
     static constexpr int E = (int)sizeof(IO);
     static constexpr int PAD = 16 / E;           // 16 bytes of padding per LDS row
-    static constexpr int SB = NP + PAD;          // row stride of the B tile
+    static constexpr int SB = NP + PAD;          // row stride of the B chunk
     static constexpr int SX = Q + PAD;           // row stride of the x^T tile
     static constexpr int SH = NP + PAD;          // row stride of the incoming state
     static constexpr int kLdsB = Q * SB * E;
@@ -83,7 +97,7 @@ struct FwdShape {
     static constexpr int kNVec = 6;              // per-token float vectors
     static constexpr int kLdsVec = kNVec * Q * 4;
     static constexpr int kLds = kLdsB + kLdsX + kLdsH + kLdsVec + 16;
-    static constexpr bool kFits = kLds <= 160 * 1024;
+    static constexpr bool kFits = kLds <= 160 * 1024 && QT <= 2 * kWaves;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -91,12 +105,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2f_fast(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// Row tile handled by `wave` in its round `k`: a snake order over the waves,
-// so that every wave gets a similar share of the causal (triangular) work.
-__device__ __forceinline__ int snake_tile(int wave, int k, int nwaves) {
-    return k * nwaves + ((k & 1) ? (nwaves - 1 - wave) : wave);
-}
 
 // Unscaled B^T fragment: lane holds B[k0 + 8*lg + e][n0 + li], e = 0..7.
 template <typename IO, int SB>
@@ -127,6 +135,65 @@ __device__ __forceinline__ typename Io<IO>::Frag scale_frag(typename Io<IO>::Fra
     return o;
 }
 
+// Registers holding one head's x chunk (units of 4 tokens x 8 channels) and,
+// in wave 0, its dt (Q/64 consecutive tokens per lane, the layout of the
+// in-chunk scan) between their global load and their use.
+template <typename IO, int P, int N, int Q>
+struct Prefetch {
+    typedef FwdShape<IO, P, N, Q> S;
+    typedef typename Io<IO>::Frag Frag;
+    static constexpr int PB = P / 8;
+    static constexpr int NUNIT = (Q / 4) * PB;
+    static constexpr int NU = (NUNIT + S::kThreads - 1) / S::kThreads;
+    static constexpr int R = Q / 64;
+    Frag x[NU][4];
+    float dt[R];
+
+    __device__ __forceinline__ void load(const FwdParams &prm, long long tok0, int q, int h, int tid) {
+        const int xs = prm.H * P;
+        const IO *xg = reinterpret_cast<const IO *>(prm.x) + tok0 * xs + h * P;
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+            const int u = tid + k * S::kThreads;
+            const int t4 = u / PB;
+            const int p0 = (u - t4 * PB) * 8;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = 4 * t4 + t;
+                x[k][t] = zero_frag<Frag>();
+                if (u < NUNIT && i < q) x[k][t] = *reinterpret_cast<const Frag *>(xg + i * xs + p0);
+            }
+        }
+        if (tid < 64) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int i = tid * R + k;
+                dt[k] = (i < q) ? prm.dt[(tok0 + i) * prm.H + h] : 0.f;
+            }
+        }
+    }
+
+    // x^T[p][i .. i+3] from 4 tokens of one channel
+    __device__ __forceinline__ void stage(IO *sX, int tid) const {
+        typedef typename Io<IO>::Half Half;
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+            const int u = tid + k * S::kThreads;
+            if (u < NUNIT) {
+                const int t4 = u / PB;
+                const int p0 = (u - t4 * PB) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    Half v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = x[k][t][e];
+                    *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + 4 * t4) = v;
+                }
+            }
+        }
+    }
+};
+
 template <typename IO, int P, int N, int Q>
 __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     typedef FwdShape<IO, P, N, Q> S;
@@ -146,301 +213,132 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     float *vRef = vEo + Q;    // s2 of the last token of each 16-tile (QT used)
     int *sTicket = reinterpret_cast<int *>(vRef + Q);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int li = lane & 15;
-    const int lg = lane >> 4;
+    int tid = threadIdx.x;
+    int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int li = lane & 15;
+    int lg = lane >> 4;
+    const int H = prm.H;
+    const int G = prm.G;
 
     if (tid == 0) sTicket[0] = atomicAdd(prm.ticket, 1);
     __syncthreads();
     const int ticket = sTicket[0];
-    const int H = prm.H;
-    const int entry = ticket / H;
-    const int h = ticket - entry * H;
+    const int per_entry = G * prm.slices;
+    const int entry = ticket / per_entry;
     if (entry >= *prm.n_chunks) return;
+    const int rem = ticket - entry * per_entry;
+    const int g = rem / prm.slices;
+    const int slice = rem - g * prm.slices;
+    const int hpg = H / G;
+    const int h_begin = g * hpg + slice * prm.heads_per_item;
+    const int h_end = min(h_begin + prm.heads_per_item, (g + 1) * hpg);
     const int4 ce = prm.chunks[entry];
     const int seq = ce.x;
     const int cloc = ce.y;
     const long long tok0 = ce.z;
     const int q = ce.w;
-    const int G = prm.G;
-    const int g = h / (H / G);
-    const float Ah = prm.A[h];
-    const float Dh = prm.D ? prm.D[h] : 0.f;
-    const int xs = H * P;    // token stride of x and y (elements)
-    const int bs = G * N;    // token stride of B and C
-    const IO *xg = reinterpret_cast<const IO *>(prm.x) + tok0 * xs + h * P;
+    const int xs = H * P;          // token stride of x and y (elements)
+    const int bs = G * N;          // token stride of B and C
     const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + g * N;
     const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + g * N;
-    IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
-    const float *dtg = prm.dt + tok0 * H + h;
 
-    // ---- issue the global loads of the B and x chunks early ----
-    constexpr int VPR = S::NP * S::E / 16;          // 16-byte vectors per B row in LDS
-    constexpr int VN = N * S::E / 16;               // vectors that hold data
-    constexpr int NVB = (Q * VPR + S::kThreads - 1) / S::kThreads;
-    i32x4 bval[NVB];
+    // ---- first head's x and dt, then the B chunk (row layout) into LDS ----
+    Prefetch<IO, P, N, Q> pf;
+    pf.load(prm, tok0, q, h_begin, tid);
+    {
+        constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
+        constexpr int VN = N * S::E / 16;        // vectors that hold data
+        constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
+        i32x4 bv[NV];
 #pragma unroll
-    for (int k = 0; k < NVB; ++k) {
-        const int v = tid + k * S::kThreads;
-        const int j = v / VPR;
-        const int c = v - j * VPR;
-        bval[k] = i32x4{0, 0, 0, 0};
-        if (v < Q * VPR && j < q && c < VN)
-            bval[k] = *reinterpret_cast<const i32x4 *>(Bg + j * bs + c * (16 / S::E));
-    }
-    // x: a unit is 4 consecutive tokens x 8 channels
-    constexpr int PB = P / 8;
-    constexpr int NUNIT = (Q / 4) * PB;
-    constexpr int NU = (NUNIT + S::kThreads - 1) / S::kThreads;
-    Frag xr[NU][4];
+        for (int k = 0; k < NV; ++k) {
+            const int u = tid + k * S::kThreads;
+            const int j = u / VPR;
+            const int c = u - j * VPR;
+            bv[k] = i32x4{0, 0, 0, 0};
+            if (u < Q * VPR && j < q && c < VN) bv[k] = *reinterpret_cast<const i32x4 *>(Bg + j * bs + c * (16 / S::E));
+        }
 #pragma unroll
-    for (int k = 0; k < NU; ++k) {
-        const int u = tid + k * S::kThreads;
-        const int it = u / PB;
-        const int p0 = (u - it * PB) * 8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int i = 4 * it + t;
-            xr[k][t] = zero_frag<Frag>();
-            if (u < NUNIT && i < q) xr[k][t] = *reinterpret_cast<const Frag *>(xg + i * xs + p0);
+        for (int k = 0; k < NV; ++k) {
+            const int u = tid + k * S::kThreads;
+            const int j = u / VPR;
+            const int c = u - j * VPR;
+            if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = bv[k];
         }
     }
 
-    // ---- in-chunk cumulative sum of dt*A (wave 0) and per-token vectors ----
-    if (wave == 0) {
-        constexpr int R = Q / 64;
-        float a[R];
-        float run = 0.f;
+    // ---- this wave's row tiles, their C rows and their C B^T tiles ----
+    // Tile Ia = wave; tile Ib = 2*kWaves-1-wave when the chunk has 2*kWaves
+    // tiles.  gtile[J] holds C B^T tile (Ia, J); gtile[GT-1-J] holds (Ib, J).
+    const int Ia = wave;
+    const int Ib = S::kTwoTiles ? 2 * S::kWaves - 1 - wave : S::QT;
+    const bool hasA = Ia < S::QT && 16 * Ia < q;
+    const bool hasB = S::kTwoTiles && 16 * Ib < q;
+    // C rows of tile I as fragments (B operand of B C^T and of H C^T)
+    auto load_c = [&](int I, Frag (&cf)[S::NK]) {
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int i = lane * R + k;
-            const float d = (i < q) ? dtg[(long long)i * H] : 0.f;
-            vDt[i] = d;
-            run += d * Ah;
-            a[k] = run;
+        for (int ks = 0; ks < S::NK; ++ks) {
+            const int n0 = ks * 32 + 8 * lg;
+            cf[ks] = zero_frag<Frag>();
+            if (16 * I + li < q && n0 < N) cf[ks] = *reinterpret_cast<const Frag *>(Cg + (16 * I + li) * bs + n0);
         }
-        float incl = run;
+    };
+    Frag cga[S::NK], cgb[S::NK];
+    load_c(hasA ? Ia : S::QT, cga);
+    load_c(hasB ? Ib : S::QT, cgb);
+    __syncthreads();  // B chunk in LDS
+    f32x4 gtile[S::GT];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        const float excl = incl - run;
-#pragma unroll
-        for (int k = 0; k < R; ++k) vS2[lane * R + k] = (excl + a[k]) * kLog2e;
-    }
-    // stage B rows while wave 0 scans
-#pragma unroll
-    for (int k = 0; k < NVB; ++k) {
-        const int v = tid + k * S::kThreads;
-        const int j = v / VPR;
-        const int c = v - j * VPR;
-        if (v < Q * VPR) *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = bval[k];
-    }
-    // stage x transposed: x^T[p][i .. i+3] from 4 tokens of one channel
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-        const int u = tid + k * S::kThreads;
-        if (u < NUNIT) {
-            const int it = u / PB;
-            const int p0 = (u - it * PB) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                Half v;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = xr[k][t][e];
-                *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + 4 * it) = v;
-            }
-        }
-    }
-    __syncthreads();
-    const float s2_last = vS2[Q - 1];
-    for (int i = tid; i < Q; i += S::kThreads) {
-        const float s2 = vS2[i];
-        const float d = vDt[i];
-        const float ref = vS2[i | 15];
-        vCol[i] = exp2f_fast(ref - s2) * d;
-        vW[i] = exp2f_fast(s2_last - s2) * d;
-        vEo[i] = exp2f_fast(s2);
-        if ((i & 15) == 15) vRef[i >> 4] = s2;
-    }
-    if constexpr (S::NP != N) {
-        for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
-            const int p = v / (S::NP - N);
-            sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
-        }
-    }
-    __syncthreads();
-
-    // ---- chunk state, transposed: S_c^T = (B^T o w) x : N x P, K = chunk ----
-    // Accumulator element r of tile (nt, pt) is S_c[p][n] with
-    // p = pt*16 + li and n = nt*16 + 4*lg + r (four consecutive state columns).
-    const int wn = wave % S::WN;
-    const int wp = wave / S::WN;
-    f32x4 accS[S::NTW][S::PTW];
-#pragma unroll
-    for (int a = 0; a < S::NTW; ++a)
-#pragma unroll
-        for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
-    if (wp < S::PT) {
-#pragma unroll 2
-        for (int ks = 0; ks < S::QK; ++ks) {
-            const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg);
-            const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg + 4);
-            Frag xf[S::PTW];
-#pragma unroll
-            for (int b = 0; b < S::PTW; ++b) {
-                const int pt = wp + b * S::WP;
-                xf[b] = zero_frag<Frag>();
-                if (pt < S::PT)
-                    xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
-            }
-#pragma unroll
-            for (int a = 0; a < S::NTW; ++a) {
-                const int nt = wn + a * S::WN;
-                if (nt < S::NT) {
-                    const Frag bt = scale_frag<IO>(load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg), wlo, whi);
-#pragma unroll
-                    for (int b = 0; b < S::PTW; ++b) {
-                        const int pt = wp + b * S::WP;
-                        if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, xf[b]);
-                    }
-                }
-            }
-        }
-    }
-
-    // ---- wait for the incoming boundary state, publish the outgoing one ----
-    // The boundary state and the progress flag are accessed with device-scope
-    // coherent operations (sc1): stores write through to the device coherence
-    // point and loads read from it, so no L2 write-back or invalidate is
-    // needed.  The producer waits until its state stores are acknowledged
-    // before the flag store; the consumer polls the flag and only then loads.
-    const int unit = seq * H + h;
-    if (cloc > 0) {
-        if (tid == 0) {
-            int it = 0;
-            while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < cloc) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++it > (1 << 22)) {
-                    atomicOr(prm.error, 1);
-                    break;
-                }
-            }
-        }
-        __syncthreads();
-    }
-    const float *hin = (cloc == 0) ? (prm.init_state ? prm.init_state + (long long)unit * P * N : nullptr)
-                                   : prm.state + (long long)unit * P * N;
-    float *hout = prm.state + (long long)unit * P * N;
-    const float alpha = exp2f_fast(s2_last);
-    if (wp < S::PT) {
-        constexpr int kDevice = 16;  // cache policy: sc1 (device scope)
-        const __amdgpu_buffer_rsrc_t rin =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(hin), 0, hin ? P * N * 4 : 0, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
-        f32x4 hv[S::NTW][S::PTW];
-#pragma unroll
-        for (int a = 0; a < S::NTW; ++a)
-#pragma unroll
-            for (int b = 0; b < S::PTW; ++b) {
-                const int nt = wn + a * S::WN, pt = wp + b * S::WP;
-                hv[a][b] = zero4();
-                if (nt < S::NT && pt < S::PT && hin)
-                    hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kDevice));
-            }
-#pragma unroll
-        for (int a = 0; a < S::NTW; ++a)
-#pragma unroll
-            for (int b = 0; b < S::PTW; ++b) {
-                const int nt = wn + a * S::WN, pt = wp + b * S::WP;
-                if (nt < S::NT && pt < S::PT) {
-                    const int p = pt * 16 + li;
-                    const int n0 = nt * 16 + 4 * lg;
-                    f32x4 o;
-                    Half hb;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        o[r] = alpha * hv[a][b][r] + accS[a][b][r];
-                        hb[r] = from_f32<IO>(hv[a][b][r]);
-                    }
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout, (p * N + n0) * 4, 0,
-                                                           kDevice);
-                    *reinterpret_cast<Half *>(sH + p * S::SH + n0) = hb;
-                }
-            }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(prm.flags + unit, cloc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    // ---- outputs, one 16-row tile at a time ----
-#pragma unroll 1
-    for (int k = 0;; ++k) {
-        const int I = snake_tile(wave, k, S::kWaves);
-        if (I >= S::QT) break;
-        const int i0 = I * 16;
-        if (i0 >= q) continue;
-        // C rows as fragments (B operand of B C^T, A operand of C H^T)
-        Frag cf[S::NK];
-        {
-            const int i = i0 + li;
+    for (int J = 0; J < S::GT; ++J) {
+        // (Ia, J) for J <= Ia, else (Ib, GT-1-J) for GT-1-J <= Ib
+        gtile[J] = zero4();
+        const bool useA = J <= Ia;
+        const int jt = useA ? J : S::GT - 1 - J;
+        const bool live = useA ? hasA : (hasB && jt <= Ib);
+        if (live) {
+            f32x4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < S::NK; ++ks) {
-                const int n0 = ks * 32 + 8 * lg;
-                cf[ks] = zero_frag<Frag>();
-                if (i < q && n0 < N) cf[ks] = *reinterpret_cast<const Frag *>(Cg + i * bs + n0);
+                const Frag bfr = *reinterpret_cast<const Frag *>(sB + (16 * jt + li) * S::SB + ks * 32 + 8 * lg);
+                acc = Io<IO>::mfma(acc, bfr, useA ? cga[ks] : cgb[ks]);
             }
+            gtile[J] = acc;
         }
-        f32x4 accO[S::PT], accY[S::PT];
-#pragma unroll
-        for (int pt = 0; pt < S::PT; ++pt) { accO[pt] = zero4(); accY[pt] = zero4(); }
-        // state read-out: C H^T
-#pragma unroll
-        for (int ks = 0; ks < S::NK; ++ks)
-#pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt) {
-                const Frag hf = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
-                accO[pt] = Io<IO>::mfma(accO[pt], cf[ks], hf);
-            }
-        // diagonal block: (C B^T o Lambda) diag(dt) x, 32 columns per step
-        const int i_row = i0 + li;
+    }
+
+    const int wn = wave % S::WN;
+    const int wp = wave / S::WN;
+
+    // Diagonal block of tile I (transposed, Y^T = x^T M^T): accumulator
+    // element r of tile pt is Y_diag[16 I + li][pt*16 + 4*lg + r].  `fromA`
+    // selects which end of gtile holds the tile's C B^T row.
+    auto diag_block = [&](auto from_a, int I, f32x4 (&accY)[S::PT]) {
+        constexpr bool fromA = decltype(from_a)::value;
+        const int i_row = 16 * I + li;
         const float s2_i = vS2[i_row];
-#pragma unroll 1
-        for (int kj = 0; kj <= I / 2; ++kj) {
-            f32x4 gt[2];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int jt = 2 * kj + half;
-                gt[half] = zero4();
-                if (jt <= I) {
+        for (int pt = 0; pt < S::PT; ++pt) accY[pt] = zero4();
 #pragma unroll
-                    for (int ks = 0; ks < S::NK; ++ks) {
-                        const Frag bfr = *reinterpret_cast<const Frag *>(sB + (jt * 16 + li) * S::SB + ks * 32 + 8 * lg);
-                        gt[half] = Io<IO>::mfma(gt[half], bfr, cf[ks]);
-                    }
-                }
-            }
-            // lane holds G[i_row][j] for j = 32 kj + 16 half + 4 lg + r
-            Frag m;
+        for (int kj = 0; kj < S::QT / 2; ++kj) {
+            if (kj > I / 2) break;
+            Frag m;  // lane holds M[i_row][j], j = 32 kj + 16 half + 4 lg + r
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int jt = 2 * kj + half;
                 const int j0 = 32 * kj + 16 * half + 4 * lg;
+                const f32x4 &gv = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
                 if (jt < I) {
                     const float rowf = exp2f_fast(s2_i - vRef[jt]);
                     const f32x4 col = *reinterpret_cast<const f32x4 *>(vCol + j0);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gt[half][r] * rowf * col[r]);
+                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * col[r]);
                 } else if (jt == I) {
                     const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
                     const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float v = gt[half][r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
+                        const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
                         m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
                     }
                 } else {
@@ -454,23 +352,221 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 const Half lo = *reinterpret_cast<const Half *>(xrp);
                 const Half hi = *reinterpret_cast<const Half *>(xrp + 16);
                 const Frag xf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                accY[pt] = Io<IO>::mfma(accY[pt], m, xf);
+                accY[pt] = Io<IO>::mfma(accY[pt], xf, m);
             }
         }
-        // y = Y_diag + exp(s_i) Y_off + D x, rows i0 + 4 lg + r
-        const f32x4 eo = *reinterpret_cast<const f32x4 *>(vEo + i0 + 4 * lg);
+    };
+    // State read-out (H C^T) and the final combination of tile I.
+    auto finish_tile = [&](int I, const Frag (&cf)[S::NK], const f32x4 (&accY)[S::PT], IO *yg, float Dh) {
+        const int i_row = 16 * I + li;
+        f32x4 accO[S::PT];
 #pragma unroll
-        for (int pt = 0; pt < S::PT; ++pt) {
-            const Half xv = *reinterpret_cast<const Half *>(sX + (pt * 16 + li) * S::SX + i0 + 4 * lg);
+        for (int pt = 0; pt < S::PT; ++pt) accO[pt] = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 4 * lg + r;
-                if (i < q) {
-                    const float yv = accY[pt][r] + eo[r] * accO[pt][r] + Dh * to_f32(xv[r]);
-                    yg[i * xs + pt * 16 + li] = from_f32<IO>(yv);
+        for (int ks = 0; ks < S::NK; ++ks)
+#pragma unroll
+            for (int pt = 0; pt < S::PT; ++pt) {
+                const Frag hf = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
+                accO[pt] = Io<IO>::mfma(accO[pt], hf, cf[ks]);
+            }
+        if (i_row < q) {
+            const float eo = vEo[i_row];
+#pragma unroll
+            for (int pt = 0; pt < S::PT; ++pt) {
+                Half yv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float xval = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + i_row]);
+                    yv[r] = from_f32<IO>(accY[pt][r] + eo * accO[pt][r] + Dh * xval);
+                }
+                *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
+            }
+        }
+    };
+
+    int *sReady = sTicket + 1;
+
+#pragma unroll 1
+    for (int h = h_begin; h < h_end; ++h) {
+        // Lane indices are made opaque per head so that per-head addresses
+        // and predicates are recomputed rather than kept live across heads.
+        asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(lg));
+        const float Ah = prm.A[h];
+        const float Dh = prm.D ? prm.D[h] : 0.f;
+        IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
+        const int unit = seq * H + h;
+
+        // ---- (1) stage x^T; wave 0: in-chunk cumulative sum and per-token vectors ----
+        pf.stage(sX, tid);
+        if (wave == 0) {
+            constexpr int R = Q / 64;
+            // one early look at the predecessor's flag (the state loads can then
+            // be issued before the compute phase)
+            int ready = 1;
+            if (cloc > 0 && lane == 0)
+                ready = __hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S::kWaves * cloc;
+            float s2[R];
+            float run = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                run += pf.dt[k] * Ah;
+                s2[k] = run;
+            }
+            float incl = run;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float v = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += v;
+            }
+            const float excl = incl - run;
+#pragma unroll
+            for (int k = 0; k < R; ++k) s2[k] = (excl + s2[k]) * kLog2e;
+            const float s2_end = __shfl(s2[R - 1], 63, 64);
+            // last token of each 16-token tile: index (i | 15), held by lane ((i | 15) / R)
+            const int ref_lane = ((lane * R) | 15) / R;
+            const float ref = __shfl(s2[R - 1], ref_lane, 64);
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int i = lane * R + k;
+                const float d = pf.dt[k];
+                vS2[i] = s2[k];
+                vDt[i] = d;
+                vCol[i] = exp2f_fast(ref - s2[k]) * d;
+                vW[i] = exp2f_fast(s2_end - s2[k]) * d;
+                vEo[i] = exp2f_fast(s2[k]);
+                if ((i & 15) == 15) vRef[i >> 4] = s2[k];
+            }
+            if (lane == 0) *sReady = ready;
+        }
+        if constexpr (S::NP != N) {
+            for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
+                const int p = v / (S::NP - N);
+                sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
+            }
+        }
+        __syncthreads();
+        const float s2_last = vS2[Q - 1];
+        const bool early = *sReady != 0;
+        // the next head's x and dt load while this head is computed
+        if (h + 1 < h_end) pf.load(prm, tok0, q, h + 1, tid);
+
+        // incoming boundary state: device-scope coherent (sc1) loads; issued now
+        // when the predecessor had already published, else after the wait below
+        const float *hin = (cloc == 0) ? (prm.init_state ? prm.init_state + (long long)unit * P * N : nullptr)
+                                       : prm.state + (long long)unit * P * N;
+        float *hout = prm.state + (long long)unit * P * N;
+        constexpr int kDevice = 16;  // cache policy: sc1 (device scope)
+        f32x4 hv[S::NTW][S::PTW];
+        auto load_state = [&]() {
+            const __amdgpu_buffer_rsrc_t rin =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(hin), 0, hin ? P * N * 4 : 0, 0x00020000);
+#pragma unroll
+            for (int a = 0; a < S::NTW; ++a)
+#pragma unroll
+                for (int b = 0; b < S::PTW; ++b) {
+                    const int nt = wn + a * S::WN, pt = wp + b * S::WP;
+                    hv[a][b] = zero4();
+                    if (wp < S::PT && nt < S::NT && pt < S::PT && hin)
+                        hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                            rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kDevice));
+                }
+        };
+        if (early) load_state();
+
+        // ---- (2) compute: chunk state and both tiles' diagonal blocks ----
+        // S_c^T = (B^T o w) x : N x P, K = chunk; accumulator element r of tile
+        // (nt, pt) is S_c[p][n] with p = pt*16 + li and n = nt*16 + 4*lg + r.
+        f32x4 accS[S::NTW][S::PTW];
+#pragma unroll
+        for (int a = 0; a < S::NTW; ++a)
+#pragma unroll
+            for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
+        if (wp < S::PT) {
+#pragma unroll 2
+            for (int ks = 0; ks < S::QK; ++ks) {
+                const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg);
+                const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg + 4);
+                Frag xf[S::PTW];
+#pragma unroll
+                for (int b = 0; b < S::PTW; ++b) {
+                    const int pt = wp + b * S::WP;
+                    xf[b] = zero_frag<Frag>();
+                    if (pt < S::PT)
+                        xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                }
+#pragma unroll
+                for (int a = 0; a < S::NTW; ++a) {
+                    const int nt = wn + a * S::WN;
+                    if (nt < S::NT) {
+                        const Frag bt = scale_frag<IO>(load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg), wlo, whi);
+#pragma unroll
+                        for (int b = 0; b < S::PTW; ++b) {
+                            const int pt = wp + b * S::WP;
+                            if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, xf[b]);
+                        }
+                    }
                 }
             }
         }
+        f32x4 accYa[S::PT], accYb[S::PT];
+        if (hasA) diag_block(std::true_type{}, Ia, accYa);
+        if (hasB) diag_block(std::false_type{}, Ib, accYb);
+
+        Frag cfa[S::NK];
+        if (hasA) load_c(Ia, cfa);
+        // ---- (3) chain: wait if needed, H_{c+1} = exp(s_last) H_c + S_c, H_c to LDS ----
+        if (!early) {
+            if (tid == 0) {
+                int it = 0;
+                while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       S::kWaves * cloc) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++it > (1 << 22)) {
+                        atomicOr(prm.error, 1);
+                        break;
+                    }
+                }
+            }
+            __syncthreads();
+            load_state();
+        }
+        const float alpha = exp2f_fast(s2_last);
+        if (wp < S::PT) {
+            const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
+#pragma unroll
+            for (int a = 0; a < S::NTW; ++a)
+#pragma unroll
+                for (int b = 0; b < S::PTW; ++b) {
+                    const int nt = wn + a * S::WN, pt = wp + b * S::WP;
+                    if (nt < S::NT && pt < S::PT) {
+                        const int p = pt * 16 + li;
+                        const int n0 = nt * 16 + 4 * lg;
+                        f32x4 o;
+                        Half hb;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            o[r] = alpha * hv[a][b][r] + accS[a][b][r];
+                            hb[r] = from_f32<IO>(hv[a][b][r]);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout, (p * N + n0) * 4,
+                                                               0, kDevice);
+                        *reinterpret_cast<Half *>(sH + p * S::SH + n0) = hb;
+                    }
+                }
+        }
+        __syncthreads();  // H_c is in LDS
+
+        // ---- (4) state read-out and outputs of both tiles ----
+        // Each wave publishes its part of H_{c+1} (one increment of the
+        // (sequence, head) counter) once its state stores are acknowledged;
+        // a successor waits for all kWaves increments.
+        Frag cfb[S::NK];
+        if (hasB) load_c(Ib, cfb);
+        if (hasA) finish_tile(Ia, cfa, accYa, yg, Dh);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
+        if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (hasB) finish_tile(Ib, cfb, accYb, yg, Dh);
+        __syncthreads();  // every wave is done with this head's LDS tiles
     }
 }
 

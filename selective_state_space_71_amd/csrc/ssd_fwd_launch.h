@@ -6,13 +6,17 @@
 
 namespace ssd {
 
+// Launches one workgroup per (chunk entry, group, head slice).  Returns true
+// when the shape is built; launches only if `launch`.
 template <typename IO, int P, int N, int Q>
-static bool fwd_try(int p, int n, int qq, const FwdParams &prm, unsigned grid, hipStream_t st,
+static bool fwd_try(int p, int n, int qq, const FwdParams &prm, long long max_entries, hipStream_t st,
                     bool launch, hipError_t *err) {
     if (p != P || n != N || qq != Q) return false;
     if constexpr (FwdShape<IO, P, N, Q>::kFits) {
         if (launch) {
-            hipLaunchKernelGGL((ssd_fwd_kernel<IO, P, N, Q>), dim3(grid), dim3(FwdShape<IO, P, N, Q>::kThreads), 0, st, prm);
+            const long long blocks = max_entries * prm.G * prm.slices;
+            hipLaunchKernelGGL((ssd_fwd_kernel<IO, P, N, Q>), dim3((unsigned)blocks),
+                               dim3(FwdShape<IO, P, N, Q>::kThreads), 0, st, prm);
             *err = hipGetLastError();
         }
         return true;
@@ -21,30 +25,25 @@ static bool fwd_try(int p, int n, int qq, const FwdParams &prm, unsigned grid, h
     }
 }
 
+#define SSD_FWD_ARGS p, n, q, prm, max_entries, st, launch, err
+#define SSD_FWD_PARAMS int p, int n, int q, const FwdParams &prm, long long max_entries, hipStream_t st, \
+                       bool launch, hipError_t *err
+
 template <typename IO, int P, int N>
-static bool fwd_try_q(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
-                      bool launch, hipError_t *err) {
-    return fwd_try<IO, P, N, 64>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try<IO, P, N, 128>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try<IO, P, N, 256>(p, n, q, prm, grid, st, launch, err);
+static bool fwd_try_q(SSD_FWD_PARAMS) {
+    return fwd_try<IO, P, N, 64>(SSD_FWD_ARGS) || fwd_try<IO, P, N, 128>(SSD_FWD_ARGS) ||
+           fwd_try<IO, P, N, 256>(SSD_FWD_ARGS);
 }
 
 template <typename IO, int P>
-static bool fwd_try_n(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
-                      bool launch, hipError_t *err) {
-    return fwd_try_q<IO, P, 16>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try_q<IO, P, 32>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try_q<IO, P, 64>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try_q<IO, P, 128>(p, n, q, prm, grid, st, launch, err);
+static bool fwd_try_n(SSD_FWD_PARAMS) {
+    return fwd_try_q<IO, P, 16>(SSD_FWD_ARGS) || fwd_try_q<IO, P, 32>(SSD_FWD_ARGS) ||
+           fwd_try_q<IO, P, 64>(SSD_FWD_ARGS) || fwd_try_q<IO, P, 128>(SSD_FWD_ARGS);
 }
 
-// Returns true when the shape is built; launches when `launch` is set.
 template <typename IO>
-static bool fwd_dispatch(int p, int n, int q, const FwdParams &prm, unsigned grid, hipStream_t st,
-                         bool launch, hipError_t *err) {
-    return fwd_try_n<IO, 16>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try_n<IO, 32>(p, n, q, prm, grid, st, launch, err) ||
-           fwd_try_n<IO, 64>(p, n, q, prm, grid, st, launch, err);
+static bool fwd_dispatch(SSD_FWD_PARAMS) {
+    return fwd_try_n<IO, 16>(SSD_FWD_ARGS) || fwd_try_n<IO, 32>(SSD_FWD_ARGS) || fwd_try_n<IO, 64>(SSD_FWD_ARGS);
 }
 
 }  // namespace ssd
