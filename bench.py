@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference kernel for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the SSD forward shards by (sequence, head) "
@@ -120,6 +123,12 @@ def main():
         ssd.chunk_scan_fwd(x, dt, A, B, C, D, chunk_len=w["chunk"], init_state=h0, y=y,
                            final_state=fin, workspace=ws)
 
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
