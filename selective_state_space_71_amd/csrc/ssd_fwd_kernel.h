@@ -216,6 +216,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     int tid = threadIdx.x;
     int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < S::kWaves);
     int li = lane & 15;
     int lg = lane >> 4;
     const int H = prm.H;
@@ -391,8 +392,6 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         // Lane indices are made opaque per head so that per-head addresses
         // and predicates are recomputed rather than kept live across heads.
         asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(lg));
-        const float Ah = prm.A[h];
-        const float Dh = prm.D ? prm.D[h] : 0.f;
         IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
         const int unit = seq * H + h;
 
@@ -400,6 +399,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         pf.stage(sX, tid);
         if (wave == 0) {
             constexpr int R = Q / 64;
+            const float Ah = prm.A[h];   // read by the scan only
             // one early look at the predecessor's flag (the state loads can then
             // be issued before the compute phase)
             int ready = 1;
@@ -531,6 +531,10 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             load_state();
         }
         const float alpha = exp2f_fast(s2_last);
+        const float Dh = prm.D ? prm.D[h] : 0.f;   // needed only by the epilogue
+        // every load issued so far (state, C rows of tile Ia, D) completes here, on
+        // all paths, so the read-out below only waits for what is issued later
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         if (wp < S::PT) {
             const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
 #pragma unroll
