@@ -106,19 +106,31 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2f_fast(float v) { return __builtin_amdgcn_exp2f(v); }
 
-// Unscaled B^T fragment: lane holds B[k0 + 8*lg + e][n0 + li], e = 0..7.
+// K-slot order.  Every contraction over chunk tokens uses the same slot
+// order: within a 32-token K step, slot e (0..7) of lane group lg holds token
+//     16 * (e / 4) + 4 * lg + e % 4,
+// which is the row order of the 16 x 16 C B^T accumulator tiles (two tiles
+// side by side).  The staged x^T stores tokens at the matching permuted
+// position (8 * lg + e within each 32-token block), so every x operand is one
+// contiguous 16-byte LDS read.
+__device__ __forceinline__ int xpos(int j) {
+    return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
+}
+
+// Unscaled B^T fragment in the K-slot order above: lane holds
+// B[k0 + 16 * (e / 4) + 4 * lg + e % 4][n0 + li], e = 0..7.
 template <typename IO, int SB>
 __device__ __forceinline__ typename Io<IO>::Frag load_bt_frag(const IO *sB, int k0, int n0, int li, int lg) {
     typename Io<IO>::Frag f;
     if constexpr (sizeof(IO) == 2) {
-        const int row = k0 + 8 * lg + (li >> 2);
+        const int row = k0 + 4 * lg + (li >> 2);
         const int col = n0 + 4 * (li & 3);
         const bf16x4 lo = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + row * SB + col));
-        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + (row + 4) * SB + col));
+        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + (row + 16) * SB + col));
         f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = sB[(k0 + 8 * lg + e) * SB + n0 + li];
+        for (int e = 0; e < 8; ++e) f[e] = sB[(k0 + 16 * (e >> 2) + 4 * lg + (e & 3)) * SB + n0 + li];
     }
     return f;
 }
@@ -149,14 +161,20 @@ struct Prefetch {
     Frag x[NU][4];
     float dt[R];
 
+    // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  Sixteen
+    // consecutive units take sixteen consecutive token groups of one channel
+    // block, so the transposing LDS writes of 16 lanes hit distinct banks.
+    static __device__ __forceinline__ int unit_t4(int u) { return (u & 15) + 16 * (u / (16 * PB)); }
+    static __device__ __forceinline__ int unit_p0(int u) { return ((u >> 4) % PB) * 8; }
+
     __device__ __forceinline__ void load(const FwdParams &prm, long long tok0, int q, int h, int tid) {
         const int xs = prm.H * P;
         const IO *xg = reinterpret_cast<const IO *>(prm.x) + tok0 * xs + h * P;
 #pragma unroll
         for (int k = 0; k < NU; ++k) {
             const int u = tid + k * S::kThreads;
-            const int t4 = u / PB;
-            const int p0 = (u - t4 * PB) * 8;
+            const int t4 = unit_t4(u);
+            const int p0 = unit_p0(u);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int i = 4 * t4 + t;
@@ -180,14 +198,15 @@ struct Prefetch {
         for (int k = 0; k < NU; ++k) {
             const int u = tid + k * S::kThreads;
             if (u < NUNIT) {
-                const int t4 = u / PB;
-                const int p0 = (u - t4 * PB) * 8;
+                const int t4 = unit_t4(u);
+                const int p0 = unit_p0(u);
+                const int pos = xpos(4 * t4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     Half v;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = x[k][t][e];
-                    *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + 4 * t4) = v;
+                    *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + pos) = v;
                 }
             }
         }
@@ -349,10 +368,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             }
 #pragma unroll
             for (int pt = 0; pt < S::PT; ++pt) {
-                const IO *xrp = sX + (pt * 16 + li) * S::SX + 32 * kj + 4 * lg;
-                const Half lo = *reinterpret_cast<const Half *>(xrp);
-                const Half hi = *reinterpret_cast<const Half *>(xrp + 16);
-                const Frag xf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const Frag xf = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + 32 * kj + 8 * lg);
                 accY[pt] = Io<IO>::mfma(accY[pt], xf, m);
             }
         }
@@ -377,7 +393,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 Half yv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float xval = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + i_row]);
+                    const float xval = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + xpos(i_row)]);
                     yv[r] = from_f32<IO>(accY[pt][r] + eo * accO[pt][r] + Dh * xval);
                 }
                 *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
@@ -484,8 +500,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         if (wp < S::PT) {
 #pragma unroll 2
             for (int ks = 0; ks < S::QK; ++ks) {
-                const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg);
-                const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 8 * lg + 4);
+                const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 4 * lg);
+                const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 16 + 4 * lg);
                 Frag xf[S::PTW];
 #pragma unroll
                 for (int b = 0; b < S::PTW; ++b) {
