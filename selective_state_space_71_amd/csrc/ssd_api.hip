@@ -20,46 +20,36 @@ bool fwd_dispatch_f32(int p, int n, int q, const FwdParams &prm, long long max_e
 // Chunk schedule.  Every (sequence, chunk index) pair becomes one entry
 // {seq, chunk index in seq, first token, length}.  Entries are ordered by
 // chunk index first and sequence second, so the predecessor of an entry
-// (same sequence, previous chunk) always has a smaller index; the forward
-// kernel hands out work in this order.  The kernel also clears the ticket,
-// the error word and the per-(sequence, head) progress flags, and writes the
-// final state of empty packed sequences (the initial state, or zero).
+// (same sequence, previous chunk) always has a smaller index.  A work item
+// is (entry, group, head slice); all items of one (sequence, group, slice)
+// chain go to the same XCD (round robin over chains), and each XCD's list
+// keeps the entry order, so an item's predecessor is always earlier in the
+// same list.  The kernel also clears the tickets, the error word and the
+// per-(sequence, head) progress flags, and writes the final state of empty
+// packed sequences (the initial state, or zero).
 struct PrepParams {
     const int *cu_seqlens;  // null for a dense batch
     int batch, seqlen, nseq, H, Q;
+    int G, slices, n_xcd;
     int state_elems;        // P * N
     int4 *chunks;
     int *n_chunks;
-    int *ticket;
+    int *tickets;           // [16] one per XCD
     int *error;
     int *flags;
+    int *items;             // per-XCD item lists, concatenated
+    int *xcd_count;         // [16]
+    int *xcd_offset;        // [16]
     int *seq_chunk_start;   // [nseq + 1] scratch (packed batches)
     const float *init_state;
     float *final_state;
 };
 
-__global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
+// Packed batch: chunk counts per sequence, their running sum, the
+// chunk-index-major table and the final state of empty sequences.
+__device__ void build_packed_schedule(const PrepParams &p) {
     const int tid = threadIdx.x;
     const int Q = p.Q;
-    for (int u = tid; u < p.nseq * p.H; u += 256) p.flags[u] = 0;
-    if (tid == 0) {
-        *p.ticket = 0;
-        *p.error = 0;
-    }
-    if (p.cu_seqlens == nullptr) {
-        const int nc = (p.seqlen + Q - 1) / Q;
-        const int total = nc * p.batch;
-        if (tid == 0) *p.n_chunks = total;
-        for (int e = tid; e < total; e += 256) {
-            const int c = e / p.batch;
-            const int s = e - c * p.batch;
-            const int start = c * Q;
-            const int len = min(Q, p.seqlen - start);
-            p.chunks[e] = make_int4(s, c, s * p.seqlen + start, len);
-        }
-        return;
-    }
-    // packed batch: chunk counts and their running sum over sequences
     if (tid == 0) {
         int acc = 0;
         for (int s = 0; s < p.nseq; ++s) {
@@ -96,6 +86,73 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
             const long long base = (long long)s * p.H * p.state_elems;
             for (long long k = tid; k < (long long)p.H * p.state_elems; k += 256)
                 p.final_state[base + k] = p.init_state ? p.init_state[base + k] : 0.f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
+    const int tid = threadIdx.x;
+    const int Q = p.Q;
+    __shared__ int cnt[16], run[16];
+    for (int u = tid; u < p.nseq * p.H; u += 256) p.flags[u] = 0;
+    if (tid < 16) {
+        p.tickets[tid] = 0;
+        cnt[tid] = 0;
+        run[tid] = 0;
+    }
+    if (tid == 0) *p.error = 0;
+    if (p.cu_seqlens == nullptr) {
+        const int nc = (p.seqlen + Q - 1) / Q;
+        const int total = nc * p.batch;
+        if (tid == 0) *p.n_chunks = total;
+        for (int e = tid; e < total; e += 256) {
+            const int c = e / p.batch;
+            const int s = e - c * p.batch;
+            const int start = c * Q;
+            const int len = min(Q, p.seqlen - start);
+            p.chunks[e] = make_int4(s, c, s * p.seqlen + start, len);
+        }
+    } else {
+        build_packed_schedule(p);
+    }
+    __syncthreads();
+    // per-XCD item lists: counts, offsets, then an order-preserving placement
+    const int GS = p.G * p.slices;
+    const int n_items = *p.n_chunks * GS;
+    auto xcd_of = [&](int i) {
+        const int e = i / GS;
+        return (p.chunks[e].x * GS + (i - e * GS)) % p.n_xcd;
+    };
+    for (int i = tid; i < n_items; i += 256) atomicAdd(&cnt[xcd_of(i)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int x = 0; x < 16; ++x) {
+            p.xcd_offset[x] = acc;
+            p.xcd_count[x] = cnt[x];
+            acc += cnt[x];
+            cnt[x] = p.xcd_offset[x];
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const unsigned long long lt = (1ull << tid) - 1ull;
+        for (int base = 0; base < n_items; base += 64) {
+            const int i = base + tid;
+            const bool valid = i < n_items;
+            const int x = valid ? xcd_of(i) : 0;
+            unsigned long long same = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const unsigned long long m = __ballot(valid && ((x >> b) & 1));
+                same &= ((x >> b) & 1) ? m : ~m;
+            }
+            const int rank = __popcll(same & lt);
+            volatile int *vrun = run;
+            if (valid) p.items[cnt[x] + vrun[x] + rank] = i;
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) vrun[x] = vrun[x] + __popcll(same);
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -205,16 +262,28 @@ bool overlap(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Compute units of the current device (cached per device id).
-int num_compute_units() {
-    static int cache[64] = {0};
+// A device attribute of the current device (cached per device id), or -1.
+int device_attr(hipDeviceAttribute_t attr, int (&cache)[64]) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
     if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    if (hipDeviceGetAttribute(&n, attr, dev) != hipSuccess || n <= 0) return -1;
     if (dev >= 0 && dev < 64) cache[dev] = n;
     return n;
+}
+
+int num_compute_units() {
+    static int cache[64] = {0};
+    return device_attr(hipDeviceAttributeMultiprocessorCount, cache);
+}
+
+// Number of XCDs (accelerator complexes, each with its own L2) of the
+// current device, clamped to [1, 16].
+int num_xcds() {
+    static int cache[64] = {0};
+    const int n = device_attr(hipDeviceAttributeNumberOfXccs, cache);
+    return n < 1 ? 1 : (n > 16 ? 16 : n);
 }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -222,18 +291,24 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct WsLayout {
-    size_t flags, chunks, scratch, state, total;
+    size_t flags, chunks, items, scratch, state, total;
     long long max_entries;
 };
 
-// Workspace: [0,256) ticket / error / entry count; per-(sequence, head)
-// flags; chunk table; packed-batch scratch; fp32 boundary-state buffer.
+// Workspace header (bytes): [0,64) one ticket per XCD, 64 error word,
+// 68 entry count, [128,192) items per XCD, [192,256) list offsets.
+constexpr size_t kWsTickets = 0, kWsError = 64, kWsEntries = 68, kWsXcdCount = 128, kWsXcdOffset = 192;
+
+// Workspace: header; per-(sequence, head) flags; chunk table; per-XCD item
+// lists (at most entries x heads items); packed-batch scratch; fp32
+// boundary-state buffer.
 bool ws_layout(const ssd_dims_t &d, int Q, bool varlen, WsLayout *w) {
     const long long nc = ((long long)d.seqlen + Q - 1) / Q;
     w->max_entries = varlen ? nc + d.nseq : nc * d.batch;
     w->flags = 256;
     w->chunks = align_up(w->flags + (size_t)d.nseq * d.nheads * 4, 256);
-    w->scratch = align_up(w->chunks + (size_t)w->max_entries * 16, 256);
+    w->items = align_up(w->chunks + (size_t)w->max_entries * 16, 256);
+    w->scratch = align_up(w->items + (size_t)w->max_entries * d.nheads * 4, 256);
     w->state = align_up(w->scratch + (size_t)(d.nseq + 1) * 4, 256);
     w->total = align_up(w->state + (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4, 256);
     return true;
@@ -353,13 +428,29 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
     pp.Q = chunk_len;
     pp.state_elems = d.headdim * d.dstate;
     pp.chunks = reinterpret_cast<int4 *>(ws + w.chunks);
-    pp.n_chunks = reinterpret_cast<int *>(ws + 8);
-    pp.ticket = reinterpret_cast<int *>(ws + 0);
-    pp.error = reinterpret_cast<int *>(ws + 4);
+    pp.n_chunks = reinterpret_cast<int *>(ws + kWsEntries);
+    pp.tickets = reinterpret_cast<int *>(ws + kWsTickets);
+    pp.error = reinterpret_cast<int *>(ws + kWsError);
     pp.flags = reinterpret_cast<int *>(ws + w.flags);
+    pp.items = reinterpret_cast<int *>(ws + w.items);
+    pp.xcd_count = reinterpret_cast<int *>(ws + kWsXcdCount);
+    pp.xcd_offset = reinterpret_cast<int *>(ws + kWsXcdOffset);
     pp.seq_chunk_start = reinterpret_cast<int *>(ws + w.scratch);
     pp.init_state = init_state;
     pp.final_state = final_state;
+
+    // head slice per work item: about eight items per compute unit, so that
+    // the workgroups sharing an XCD walk many different heads at a time
+    const int cus = num_compute_units();
+    if (cus <= 0) return SSD_ERR_HIP;
+    const int hpg = d.nheads / d.ngroups;
+    const long long want = 8LL * cus;
+    long long hs = (w.max_entries * d.nheads + want - 1) / want;
+    hs = hs < 1 ? 1 : (hs > hpg ? hpg : hs);
+    const int slices = (int)((hpg + hs - 1) / hs);
+    pp.G = d.ngroups;
+    pp.slices = slices;
+    pp.n_xcd = num_xcds();
     hipLaunchKernelGGL(ssd::ssd_prep_kernel, dim3(1), dim3(256), 0, s, pp);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
 
@@ -375,20 +466,17 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
     fp.state = final_state ? final_state : reinterpret_cast<float *>(ws + w.state);
     fp.chunks = pp.chunks;
     fp.n_chunks = pp.n_chunks;
-    fp.ticket = pp.ticket;
+    fp.tickets = pp.tickets;
+    fp.items = pp.items;
+    fp.xcd_count = pp.xcd_count;
+    fp.xcd_offset = pp.xcd_offset;
+    fp.n_xcd = pp.n_xcd;
     fp.flags = pp.flags;
     fp.error = pp.error;
     fp.H = d.nheads;
     fp.G = d.ngroups;
-    // head slice per workgroup: about two workgroups per compute unit
-    const int cus = num_compute_units();
-    if (cus <= 0) return SSD_ERR_HIP;
-    const int hpg = d.nheads / d.ngroups;
-    const long long want = 2LL * cus;
-    long long hs = (w.max_entries * d.nheads + want - 1) / want;
-    hs = hs < 1 ? 1 : (hs > hpg ? hpg : hs);
     fp.heads_per_item = (int)hs;
-    fp.slices = (int)((hpg + hs - 1) / hs);
+    fp.slices = slices;
     hipError_t err = hipSuccess;
     const bool ok = (io == SSD_BF16)
                         ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, fp, w.max_entries, s, true, &err)
@@ -403,7 +491,7 @@ ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream) {
     int word = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipStreamSynchronize(s) != hipSuccess) return SSD_ERR_HIP;
-    if (hipMemcpy(&word, static_cast<const char *>(workspace) + 4, sizeof(int), hipMemcpyDeviceToHost) !=
+    if (hipMemcpy(&word, static_cast<const char *>(workspace) + kWsError, sizeof(int), hipMemcpyDeviceToHost) !=
         hipSuccess)
         return SSD_ERR_HIP;
     return word ? SSD_ERR_DEVICE : SSD_OK;

@@ -21,15 +21,19 @@
 // wave's C rows stay in registers while the workgroup walks over its heads;
 // per head only x and dt are loaded (prefetched during the previous head).
 //
-// Chain.  Workgroups take tickets from a global counter; tickets follow the
-// chunk schedule, which is chunk-index-major, so the workgroup holding chunk
-// c-1 of the same (sequence, head slice) always started earlier and walks the
+// Chain.  Work items (chunk entry, group, head slice) are listed per XCD:
+// all chunks of one (sequence, group, slice) chain belong to the same XCD, and
+// each list is in chunk-index-major order.  A workgroup reads its XCD id and
+// takes tickets from that XCD's counter until the list is exhausted, so the
+// workgroup holding chunk c-1 of a chain took its ticket earlier and walks the
 // heads in the same order: the chain cannot deadlock.  For each head the
-// workgroup forms S_c first, then waits for the predecessor's boundary state
-// (a progress flag per (sequence, head)), computes the diagonal block of its
-// first tile while the state loads are in flight, publishes H_{c+1}, and
-// finishes the outputs.  The state buffer is the caller's final_state (or
-// workspace); it ends up holding the final state.
+// workgroup forms S_c and the diagonal blocks, then waits for the
+// predecessor's boundary state (a counter per (sequence, head) that each of
+// the predecessor's waves increments once its part of H_c is stored), updates
+// it and hands H_{c+1} on.  Producer and consumer share the XCD's L2, so the
+// state moves with ordinary stores and L1-bypassing loads.  The state buffer
+// is the caller's final_state (or workspace); it ends up holding the final
+// state.
 //
 // Numerics.  All decays are products of factors <= 1 (A <= 0, dt >= 0):
 // for a 16 x 16 tile (I, J) below the diagonal,
@@ -58,8 +62,12 @@ struct FwdParams {
     float *state;             // boundary-state buffer; holds the final state at the end
     const int4 *chunks;       // {seq, chunk index in seq, first token, length}
     const int *n_chunks;      // number of valid chunk entries
-    int *ticket;
-    int *flags;               // per (sequence, head): chunks whose state is published
+    int *tickets;             // one counter per XCD
+    const int *items;         // per-XCD work-item lists, concatenated
+    const int *xcd_count;     // items per XCD
+    const int *xcd_offset;    // start of each XCD's list
+    int n_xcd;
+    int *flags;               // per (sequence, head): published state parts (kWaves per chunk)
     int *error;
     int H, G;
     int heads_per_item;       // head slice length (the last slice of a group may be shorter)
@@ -241,352 +249,366 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     const int H = prm.H;
     const int G = prm.G;
 
-    if (tid == 0) sTicket[0] = atomicAdd(prm.ticket, 1);
-    __syncthreads();
-    const int ticket = sTicket[0];
-    const int per_entry = G * prm.slices;
-    const int entry = ticket / per_entry;
-    if (entry >= *prm.n_chunks) return;
-    const int rem = ticket - entry * per_entry;
-    const int g = rem / prm.slices;
-    const int slice = rem - g * prm.slices;
-    const int hpg = H / G;
-    const int h_begin = g * hpg + slice * prm.heads_per_item;
-    const int h_end = min(h_begin + prm.heads_per_item, (g + 1) * hpg);
-    const int4 ce = prm.chunks[entry];
-    const int seq = ce.x;
-    const int cloc = ce.y;
-    const long long tok0 = ce.z;
-    const int q = ce.w;
-    const int xs = H * P;          // token stride of x and y (elements)
-    const int bs = G * N;          // token stride of B and C
-    const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + g * N;
-    const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + g * N;
-
-    // ---- first head's x and dt, then the B chunk (row layout) into LDS ----
-    Prefetch<IO, P, N, Q> pf;
-    pf.load(prm, tok0, q, h_begin, tid);
-    {
-        constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
-        constexpr int VN = N * S::E / 16;        // vectors that hold data
-        constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
-        i32x4 bv[NV];
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int u = tid + k * S::kThreads;
-            const int j = u / VPR;
-            const int c = u - j * VPR;
-            bv[k] = i32x4{0, 0, 0, 0};
-            if (u < Q * VPR && j < q && c < VN) bv[k] = *reinterpret_cast<const i32x4 *>(Bg + j * bs + c * (16 / S::E));
-        }
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int u = tid + k * S::kThreads;
-            const int j = u / VPR;
-            const int c = u - j * VPR;
-            if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = bv[k];
-        }
-    }
-
-    // ---- this wave's row tiles, their C rows and their C B^T tiles ----
-    // Tile Ia = wave; tile Ib = 2*kWaves-1-wave when the chunk has 2*kWaves
-    // tiles.  gtile[J] holds C B^T tile (Ia, J); gtile[GT-1-J] holds (Ib, J).
-    const int Ia = wave;
-    const int Ib = S::kTwoTiles ? 2 * S::kWaves - 1 - wave : S::QT;
-    const bool hasA = Ia < S::QT && 16 * Ia < q;
-    const bool hasB = S::kTwoTiles && 16 * Ib < q;
-    // C rows of tile I as fragments (B operand of B C^T and of H C^T)
-    auto load_c = [&](int I, Frag (&cf)[S::NK]) {
-#pragma unroll
-        for (int ks = 0; ks < S::NK; ++ks) {
-            const int n0 = ks * 32 + 8 * lg;
-            cf[ks] = zero_frag<Frag>();
-            if (16 * I + li < q && n0 < N) cf[ks] = *reinterpret_cast<const Frag *>(Cg + (16 * I + li) * bs + n0);
-        }
-    };
-    Frag cga[S::NK], cgb[S::NK];
-    load_c(hasA ? Ia : S::QT, cga);
-    load_c(hasB ? Ib : S::QT, cgb);
-    __syncthreads();  // B chunk in LDS
-    f32x4 gtile[S::GT];
-#pragma unroll
-    for (int J = 0; J < S::GT; ++J) {
-        // (Ia, J) for J <= Ia, else (Ib, GT-1-J) for GT-1-J <= Ib
-        gtile[J] = zero4();
-        const bool useA = J <= Ia;
-        const int jt = useA ? J : S::GT - 1 - J;
-        const bool live = useA ? hasA : (hasB && jt <= Ib);
-        if (live) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < S::NK; ++ks) {
-                const Frag bfr = *reinterpret_cast<const Frag *>(sB + (16 * jt + li) * S::SB + ks * 32 + 8 * lg);
-                acc = Io<IO>::mfma(acc, bfr, useA ? cga[ks] : cgb[ks]);
-            }
-            gtile[J] = acc;
-        }
-    }
-
-    const int wn = wave % S::WN;
-    const int wp = wave / S::WN;
-
-    // Diagonal block of tile I (transposed, Y^T = x^T M^T): accumulator
-    // element r of tile pt is Y_diag[16 I + li][pt*16 + 4*lg + r].  `fromA`
-    // selects which end of gtile holds the tile's C B^T row.
-    auto diag_block = [&](auto from_a, int I, f32x4 (&accY)[S::PT]) {
-        constexpr bool fromA = decltype(from_a)::value;
-        const int i_row = 16 * I + li;
-        const float s2_i = vS2[i_row];
-#pragma unroll
-        for (int pt = 0; pt < S::PT; ++pt) accY[pt] = zero4();
-#pragma unroll
-        for (int kj = 0; kj < S::QT / 2; ++kj) {
-            if (kj > I / 2) break;
-            Frag m;  // lane holds M[i_row][j], j = 32 kj + 16 half + 4 lg + r
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int jt = 2 * kj + half;
-                const int j0 = 32 * kj + 16 * half + 4 * lg;
-                const f32x4 &gv = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
-                if (jt < I) {
-                    const float rowf = exp2f_fast(s2_i - vRef[jt]);
-                    const f32x4 col = *reinterpret_cast<const f32x4 *>(vCol + j0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * col[r]);
-                } else if (jt == I) {
-                    const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
-                    const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
-                        m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(0.f);
-                }
-            }
-#pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt) {
-                const Frag xf = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + 32 * kj + 8 * lg);
-                accY[pt] = Io<IO>::mfma(accY[pt], xf, m);
-            }
-        }
-    };
-    // State read-out (H C^T) and the final combination of tile I.
-    auto finish_tile = [&](int I, const Frag (&cf)[S::NK], const f32x4 (&accY)[S::PT], IO *yg, float Dh) {
-        const int i_row = 16 * I + li;
-        f32x4 accO[S::PT];
-#pragma unroll
-        for (int pt = 0; pt < S::PT; ++pt) accO[pt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < S::NK; ++ks)
-#pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt) {
-                const Frag hf = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
-                accO[pt] = Io<IO>::mfma(accO[pt], hf, cf[ks]);
-            }
-        if (i_row < q) {
-            const float eo = vEo[i_row];
-#pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt) {
-                Half yv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float xval = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + xpos(i_row)]);
-                    yv[r] = from_f32<IO>(accY[pt][r] + eo * accO[pt][r] + Dh * xval);
-                }
-                *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
-            }
-        }
-    };
-
-    int *sReady = sTicket + 1;
-
+    // This workgroup's XCD; it only takes items of that XCD's list, so every
+    // chunk of a (sequence, head) chain runs on one XCD and the boundary state
+    // passes through that XCD's L2.
+    const int xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 15) % prm.n_xcd;  // HW_REG_XCC_ID
 #pragma unroll 1
-    for (int h = h_begin; h < h_end; ++h) {
-        // Lane indices are made opaque per head so that per-head addresses
-        // and predicates are recomputed rather than kept live across heads.
-        asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(lg));
-        IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
-        const int unit = seq * H + h;
-
-        // ---- (1) stage x^T; wave 0: in-chunk cumulative sum and per-token vectors ----
-        pf.stage(sX, tid);
-        if (wave == 0) {
-            constexpr int R = Q / 64;
-            const float Ah = prm.A[h];   // read by the scan only
-            // one early look at the predecessor's flag (the state loads can then
-            // be issued before the compute phase)
-            int ready = 1;
-            if (cloc > 0 && lane == 0)
-                ready = __hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S::kWaves * cloc;
-            float s2[R];
-            float run = 0.f;
-#pragma unroll
-            for (int k = 0; k < R; ++k) {
-                run += pf.dt[k] * Ah;
-                s2[k] = run;
-            }
-            float incl = run;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float v = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += v;
-            }
-            const float excl = incl - run;
-#pragma unroll
-            for (int k = 0; k < R; ++k) s2[k] = (excl + s2[k]) * kLog2e;
-            const float s2_end = __shfl(s2[R - 1], 63, 64);
-            // last token of each 16-token tile: index (i | 15), held by lane ((i | 15) / R)
-            const int ref_lane = ((lane * R) | 15) / R;
-            const float ref = __shfl(s2[R - 1], ref_lane, 64);
-#pragma unroll
-            for (int k = 0; k < R; ++k) {
-                const int i = lane * R + k;
-                const float d = pf.dt[k];
-                vS2[i] = s2[k];
-                vDt[i] = d;
-                vCol[i] = exp2f_fast(ref - s2[k]) * d;
-                vW[i] = exp2f_fast(s2_end - s2[k]) * d;
-                vEo[i] = exp2f_fast(s2[k]);
-                if ((i & 15) == 15) vRef[i >> 4] = s2[k];
-            }
-            if (lane == 0) *sReady = ready;
-        }
-        if constexpr (S::NP != N) {
-            for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
-                const int p = v / (S::NP - N);
-                sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
-            }
+    for (;;) {
+        if (tid == 0) {
+            const int t = atomicAdd(prm.tickets + xcd, 1);
+            sTicket[0] = t < prm.xcd_count[xcd] ? prm.items[prm.xcd_offset[xcd] + t] : -1;
         }
         __syncthreads();
-        const float s2_last = vS2[Q - 1];
-        const bool early = *sReady != 0;
-        // the next head's x and dt load while this head is computed
-        if (h + 1 < h_end) pf.load(prm, tok0, q, h + 1, tid);
+        const int ticket = sTicket[0];
+        if (ticket < 0) break;
+        const int per_entry = G * prm.slices;
+        const int entry = ticket / per_entry;
+        const int rem = ticket - entry * per_entry;
+        const int g = rem / prm.slices;
+        const int slice = rem - g * prm.slices;
+        const int hpg = H / G;
+        const int h_begin = g * hpg + slice * prm.heads_per_item;
+        const int h_end = min(h_begin + prm.heads_per_item, (g + 1) * hpg);
+        const int4 ce = prm.chunks[entry];
+        const int seq = ce.x;
+        const int cloc = ce.y;
+        const long long tok0 = ce.z;
+        const int q = ce.w;
+        const int xs = H * P;          // token stride of x and y (elements)
+        const int bs = G * N;          // token stride of B and C
+        const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + g * N;
+        const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + g * N;
 
-        // incoming boundary state: device-scope coherent (sc1) loads; issued now
-        // when the predecessor had already published, else after the wait below
-        const float *hin = (cloc == 0) ? (prm.init_state ? prm.init_state + (long long)unit * P * N : nullptr)
-                                       : prm.state + (long long)unit * P * N;
-        float *hout = prm.state + (long long)unit * P * N;
-        constexpr int kDevice = 16;  // cache policy: sc1 (device scope)
-        f32x4 hv[S::NTW][S::PTW];
-        auto load_state = [&]() {
-            const __amdgpu_buffer_rsrc_t rin =
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(hin), 0, hin ? P * N * 4 : 0, 0x00020000);
-#pragma unroll
-            for (int a = 0; a < S::NTW; ++a)
-#pragma unroll
-                for (int b = 0; b < S::PTW; ++b) {
-                    const int nt = wn + a * S::WN, pt = wp + b * S::WP;
-                    hv[a][b] = zero4();
-                    if (wp < S::PT && nt < S::NT && pt < S::PT && hin)
-                        hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kDevice));
-                }
-        };
-        if (early) load_state();
-
-        // ---- (2) compute: chunk state and both tiles' diagonal blocks ----
-        // S_c^T = (B^T o w) x : N x P, K = chunk; accumulator element r of tile
-        // (nt, pt) is S_c[p][n] with p = pt*16 + li and n = nt*16 + 4*lg + r.
-        f32x4 accS[S::NTW][S::PTW];
-#pragma unroll
-        for (int a = 0; a < S::NTW; ++a)
-#pragma unroll
-            for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
-        if (wp < S::PT) {
-#pragma unroll 2
-            for (int ks = 0; ks < S::QK; ++ks) {
-                const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 4 * lg);
-                const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 16 + 4 * lg);
-                Frag xf[S::PTW];
-#pragma unroll
-                for (int b = 0; b < S::PTW; ++b) {
-                    const int pt = wp + b * S::WP;
-                    xf[b] = zero_frag<Frag>();
-                    if (pt < S::PT)
-                        xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
-                }
-#pragma unroll
-                for (int a = 0; a < S::NTW; ++a) {
-                    const int nt = wn + a * S::WN;
-                    if (nt < S::NT) {
-                        const Frag bt = scale_frag<IO>(load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg), wlo, whi);
-#pragma unroll
-                        for (int b = 0; b < S::PTW; ++b) {
-                            const int pt = wp + b * S::WP;
-                            if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, xf[b]);
-                        }
-                    }
-                }
+        // ---- first head's x and dt, then the B chunk (row layout) into LDS ----
+        Prefetch<IO, P, N, Q> pf;
+        pf.load(prm, tok0, q, h_begin, tid);
+        {
+            constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
+            constexpr int VN = N * S::E / 16;        // vectors that hold data
+            constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
+            i32x4 bv[NV];
+    #pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int u = tid + k * S::kThreads;
+                const int j = u / VPR;
+                const int c = u - j * VPR;
+                bv[k] = i32x4{0, 0, 0, 0};
+                if (u < Q * VPR && j < q && c < VN) bv[k] = *reinterpret_cast<const i32x4 *>(Bg + j * bs + c * (16 / S::E));
+            }
+    #pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int u = tid + k * S::kThreads;
+                const int j = u / VPR;
+                const int c = u - j * VPR;
+                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = bv[k];
             }
         }
-        f32x4 accYa[S::PT], accYb[S::PT];
-        if (hasA) diag_block(std::true_type{}, Ia, accYa);
-        if (hasB) diag_block(std::false_type{}, Ib, accYb);
 
-        Frag cfa[S::NK];
-        if (hasA) load_c(Ia, cfa);
-        // ---- (3) chain: wait if needed, H_{c+1} = exp(s_last) H_c + S_c, H_c to LDS ----
-        if (!early) {
-            if (tid == 0) {
-                int it = 0;
-                while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                       S::kWaves * cloc) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++it > (1 << 22)) {
-                        atomicOr(prm.error, 1);
-                        break;
+        // ---- this wave's row tiles, their C rows and their C B^T tiles ----
+        // Tile Ia = wave; tile Ib = 2*kWaves-1-wave when the chunk has 2*kWaves
+        // tiles.  gtile[J] holds C B^T tile (Ia, J); gtile[GT-1-J] holds (Ib, J).
+        const int Ia = wave;
+        const int Ib = S::kTwoTiles ? 2 * S::kWaves - 1 - wave : S::QT;
+        const bool hasA = Ia < S::QT && 16 * Ia < q;
+        const bool hasB = S::kTwoTiles && 16 * Ib < q;
+        // C rows of tile I as fragments (B operand of B C^T and of H C^T)
+        auto load_c = [&](int I, Frag (&cf)[S::NK]) {
+    #pragma unroll
+            for (int ks = 0; ks < S::NK; ++ks) {
+                const int n0 = ks * 32 + 8 * lg;
+                cf[ks] = zero_frag<Frag>();
+                if (16 * I + li < q && n0 < N) cf[ks] = *reinterpret_cast<const Frag *>(Cg + (16 * I + li) * bs + n0);
+            }
+        };
+        Frag cga[S::NK], cgb[S::NK];
+        load_c(hasA ? Ia : S::QT, cga);
+        load_c(hasB ? Ib : S::QT, cgb);
+        __syncthreads();  // B chunk in LDS
+        f32x4 gtile[S::GT];
+    #pragma unroll
+        for (int J = 0; J < S::GT; ++J) {
+            // (Ia, J) for J <= Ia, else (Ib, GT-1-J) for GT-1-J <= Ib
+            gtile[J] = zero4();
+            const bool useA = J <= Ia;
+            const int jt = useA ? J : S::GT - 1 - J;
+            const bool live = useA ? hasA : (hasB && jt <= Ib);
+            if (live) {
+                f32x4 acc = zero4();
+    #pragma unroll
+                for (int ks = 0; ks < S::NK; ++ks) {
+                    const Frag bfr = *reinterpret_cast<const Frag *>(sB + (16 * jt + li) * S::SB + ks * 32 + 8 * lg);
+                    acc = Io<IO>::mfma(acc, bfr, useA ? cga[ks] : cgb[ks]);
+                }
+                gtile[J] = acc;
+            }
+        }
+
+        const int wn = wave % S::WN;
+        const int wp = wave / S::WN;
+
+        // Diagonal block of tile I (transposed, Y^T = x^T M^T): accumulator
+        // element r of tile pt is Y_diag[16 I + li][pt*16 + 4*lg + r].  `fromA`
+        // selects which end of gtile holds the tile's C B^T row.
+        auto diag_block = [&](auto from_a, int I, f32x4 (&accY)[S::PT]) {
+            constexpr bool fromA = decltype(from_a)::value;
+            const int i_row = 16 * I + li;
+            const float s2_i = vS2[i_row];
+    #pragma unroll
+            for (int pt = 0; pt < S::PT; ++pt) accY[pt] = zero4();
+    #pragma unroll
+            for (int kj = 0; kj < S::QT / 2; ++kj) {
+                if (kj > I / 2) break;
+                Frag m;  // lane holds M[i_row][j], j = 32 kj + 16 half + 4 lg + r
+    #pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int jt = 2 * kj + half;
+                    const int j0 = 32 * kj + 16 * half + 4 * lg;
+                    const f32x4 &gv = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
+                    if (jt < I) {
+                        const float rowf = exp2f_fast(s2_i - vRef[jt]);
+                        const f32x4 col = *reinterpret_cast<const f32x4 *>(vCol + j0);
+    #pragma unroll
+                        for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * col[r]);
+                    } else if (jt == I) {
+                        const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
+                        const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
+    #pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
+                            m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
+                        }
+                    } else {
+    #pragma unroll
+                        for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(0.f);
                     }
+                }
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt) {
+                    const Frag xf = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + 32 * kj + 8 * lg);
+                    accY[pt] = Io<IO>::mfma(accY[pt], xf, m);
+                }
+            }
+        };
+        // State read-out (H C^T) and the final combination of tile I.
+        auto finish_tile = [&](int I, const Frag (&cf)[S::NK], const f32x4 (&accY)[S::PT], IO *yg, float Dh) {
+            const int i_row = 16 * I + li;
+            f32x4 accO[S::PT];
+    #pragma unroll
+            for (int pt = 0; pt < S::PT; ++pt) accO[pt] = zero4();
+    #pragma unroll
+            for (int ks = 0; ks < S::NK; ++ks)
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt) {
+                    const Frag hf = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
+                    accO[pt] = Io<IO>::mfma(accO[pt], hf, cf[ks]);
+                }
+            if (i_row < q) {
+                const float eo = vEo[i_row];
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt) {
+                    Half yv;
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float xval = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + xpos(i_row)]);
+                        yv[r] = from_f32<IO>(accY[pt][r] + eo * accO[pt][r] + Dh * xval);
+                    }
+                    *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
+                }
+            }
+        };
+
+        int *sReady = sTicket + 1;
+
+    #pragma unroll 1
+        for (int h = h_begin; h < h_end; ++h) {
+            // Lane indices are made opaque per head so that per-head addresses
+            // and predicates are recomputed rather than kept live across heads.
+            asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(lg));
+            IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
+            const int unit = seq * H + h;
+
+            // ---- (1) stage x^T; wave 0: in-chunk cumulative sum and per-token vectors ----
+            pf.stage(sX, tid);
+            if (wave == 0) {
+                constexpr int R = Q / 64;
+                const float Ah = prm.A[h];   // read by the scan only
+                // one early look at the predecessor's flag (the state loads can then
+                // be issued before the compute phase)
+                int ready = 1;
+                if (cloc > 0 && lane == 0)
+                    ready = __hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S::kWaves * cloc;
+                float s2[R];
+                float run = 0.f;
+    #pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    run += pf.dt[k] * Ah;
+                    s2[k] = run;
+                }
+                float incl = run;
+    #pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float v = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += v;
+                }
+                const float excl = incl - run;
+    #pragma unroll
+                for (int k = 0; k < R; ++k) s2[k] = (excl + s2[k]) * kLog2e;
+                const float s2_end = __shfl(s2[R - 1], 63, 64);
+                // last token of each 16-token tile: index (i | 15), held by lane ((i | 15) / R)
+                const int ref_lane = ((lane * R) | 15) / R;
+                const float ref = __shfl(s2[R - 1], ref_lane, 64);
+    #pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    const int i = lane * R + k;
+                    const float d = pf.dt[k];
+                    vS2[i] = s2[k];
+                    vDt[i] = d;
+                    vCol[i] = exp2f_fast(ref - s2[k]) * d;
+                    vW[i] = exp2f_fast(s2_end - s2[k]) * d;
+                    vEo[i] = exp2f_fast(s2[k]);
+                    if ((i & 15) == 15) vRef[i >> 4] = s2[k];
+                }
+                if (lane == 0) *sReady = ready;
+            }
+            if constexpr (S::NP != N) {
+                for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
+                    const int p = v / (S::NP - N);
+                    sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
                 }
             }
             __syncthreads();
-            load_state();
-        }
-        const float alpha = exp2f_fast(s2_last);
-        const float Dh = prm.D ? prm.D[h] : 0.f;   // needed only by the epilogue
-        // every load issued so far (state, C rows of tile Ia, D) completes here, on
-        // all paths, so the read-out below only waits for what is issued later
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        if (wp < S::PT) {
-            const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
-#pragma unroll
+            const float s2_last = vS2[Q - 1];
+            const bool early = *sReady != 0;
+            // the next head's x and dt load while this head is computed
+            if (h + 1 < h_end) pf.load(prm, tok0, q, h + 1, tid);
+
+            // incoming boundary state, issued now
+            // when the predecessor had already published, else after the wait below
+            const float *hin = (cloc == 0) ? (prm.init_state ? prm.init_state + (long long)unit * P * N : nullptr)
+                                           : prm.state + (long long)unit * P * N;
+            float *hout = prm.state + (long long)unit * P * N;
+            // Cache policy of the hand-off: the stores are ordinary, so H_{c+1}
+            // stays in this XCD's L2 (write-back); the loads are device scope
+            // (sc1), which skips the compute unit's L1 (it may hold an older
+            // version of these in-place lines) and is served by the same L2.
+            constexpr int kStateLoad = 16;   // sc1
+            f32x4 hv[S::NTW][S::PTW];
+            auto load_state = [&]() {
+                const __amdgpu_buffer_rsrc_t rin =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(hin), 0, hin ? P * N * 4 : 0, 0x00020000);
+    #pragma unroll
+                for (int a = 0; a < S::NTW; ++a)
+    #pragma unroll
+                    for (int b = 0; b < S::PTW; ++b) {
+                        const int nt = wn + a * S::WN, pt = wp + b * S::WP;
+                        hv[a][b] = zero4();
+                        if (wp < S::PT && nt < S::NT && pt < S::PT && hin)
+                            hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kStateLoad));
+                    }
+            };
+            if (early) load_state();
+
+            // ---- (2) compute: chunk state and both tiles' diagonal blocks ----
+            // S_c^T = (B^T o w) x : N x P, K = chunk; accumulator element r of tile
+            // (nt, pt) is S_c[p][n] with p = pt*16 + li and n = nt*16 + 4*lg + r.
+            f32x4 accS[S::NTW][S::PTW];
+    #pragma unroll
             for (int a = 0; a < S::NTW; ++a)
-#pragma unroll
-                for (int b = 0; b < S::PTW; ++b) {
-                    const int nt = wn + a * S::WN, pt = wp + b * S::WP;
-                    if (nt < S::NT && pt < S::PT) {
-                        const int p = pt * 16 + li;
-                        const int n0 = nt * 16 + 4 * lg;
-                        f32x4 o;
-                        Half hb;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            o[r] = alpha * hv[a][b][r] + accS[a][b][r];
-                            hb[r] = from_f32<IO>(hv[a][b][r]);
+    #pragma unroll
+                for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
+            if (wp < S::PT) {
+    #pragma unroll 2
+                for (int ks = 0; ks < S::QK; ++ks) {
+                    const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 4 * lg);
+                    const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 16 + 4 * lg);
+                    Frag xf[S::PTW];
+    #pragma unroll
+                    for (int b = 0; b < S::PTW; ++b) {
+                        const int pt = wp + b * S::WP;
+                        xf[b] = zero_frag<Frag>();
+                        if (pt < S::PT)
+                            xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                    }
+    #pragma unroll
+                    for (int a = 0; a < S::NTW; ++a) {
+                        const int nt = wn + a * S::WN;
+                        if (nt < S::NT) {
+                            const Frag bt = scale_frag<IO>(load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg), wlo, whi);
+    #pragma unroll
+                            for (int b = 0; b < S::PTW; ++b) {
+                                const int pt = wp + b * S::WP;
+                                if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, xf[b]);
+                            }
                         }
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout, (p * N + n0) * 4,
-                                                               0, kDevice);
-                        *reinterpret_cast<Half *>(sH + p * S::SH + n0) = hb;
                     }
                 }
-        }
-        __syncthreads();  // H_c is in LDS
+            }
+            f32x4 accYa[S::PT], accYb[S::PT];
+            if (hasA) diag_block(std::true_type{}, Ia, accYa);
+            if (hasB) diag_block(std::false_type{}, Ib, accYb);
 
-        // ---- (4) state read-out and outputs of both tiles ----
-        // Each wave publishes its part of H_{c+1} (one increment of the
-        // (sequence, head) counter) once its state stores are acknowledged;
-        // a successor waits for all kWaves increments.
-        Frag cfb[S::NK];
-        if (hasB) load_c(Ib, cfb);
-        if (hasA) finish_tile(Ia, cfa, accYa, yg, Dh);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
-        if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (hasB) finish_tile(Ib, cfb, accYb, yg, Dh);
-        __syncthreads();  // every wave is done with this head's LDS tiles
+            Frag cfa[S::NK];
+            if (hasA) load_c(Ia, cfa);
+            // ---- (3) chain: wait if needed, H_{c+1} = exp(s_last) H_c + S_c, H_c to LDS ----
+            if (!early) {
+                if (tid == 0) {
+                    int it = 0;
+                    while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                           S::kWaves * cloc) {
+                        __builtin_amdgcn_s_sleep(1);
+                        if (++it > (1 << 22)) {
+                            atomicOr(prm.error, 1);
+                            break;
+                        }
+                    }
+                }
+                __syncthreads();
+                load_state();
+            }
+            const float alpha = exp2f_fast(s2_last);
+            const float Dh = prm.D ? prm.D[h] : 0.f;   // needed only by the epilogue
+            // every load issued so far (state, C rows of tile Ia, D) completes here, on
+            // all paths, so the read-out below only waits for what is issued later
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if (wp < S::PT) {
+                const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
+    #pragma unroll
+                for (int a = 0; a < S::NTW; ++a)
+    #pragma unroll
+                    for (int b = 0; b < S::PTW; ++b) {
+                        const int nt = wn + a * S::WN, pt = wp + b * S::WP;
+                        if (nt < S::NT && pt < S::PT) {
+                            const int p = pt * 16 + li;
+                            const int n0 = nt * 16 + 4 * lg;
+                            f32x4 o;
+                            Half hb;
+    #pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                o[r] = alpha * hv[a][b][r] + accS[a][b][r];
+                                hb[r] = from_f32<IO>(hv[a][b][r]);
+                            }
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout, (p * N + n0) * 4,
+                                                                   0, 0);
+                            *reinterpret_cast<Half *>(sH + p * S::SH + n0) = hb;
+                        }
+                    }
+            }
+            __syncthreads();  // H_c is in LDS
+
+            // ---- (4) state read-out and outputs of both tiles ----
+            // Each wave publishes its part of H_{c+1} (one increment of the
+            // (sequence, head) counter) once its state stores are acknowledged;
+            // a successor waits for all kWaves increments.
+            Frag cfb[S::NK];
+            if (hasB) load_c(Ib, cfb);
+            if (hasA) finish_tile(Ia, cfa, accYa, yg, Dh);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
+            if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (hasB) finish_tile(Ib, cfb, accYb, yg, Dh);
+            __syncthreads();  // every wave is done with this head's LDS tiles
+        }
     }
 }
 

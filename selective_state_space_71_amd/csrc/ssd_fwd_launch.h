@@ -6,15 +6,18 @@
 
 namespace ssd {
 
-// Launches one workgroup per (chunk entry, group, head slice).  Returns true
-// when the shape is built; launches only if `launch`.
+// Launches one workgroup per possible work item (chunk entry, group, head
+// slice), rounded up to a multiple of the XCD count; workgroups loop over
+// their XCD's item list.  Returns true when the shape is built; launches only
+// if `launch`.
 template <typename IO, int P, int N, int Q>
 static bool fwd_try(int p, int n, int qq, const FwdParams &prm, long long max_entries, hipStream_t st,
                     bool launch, hipError_t *err) {
     if (p != P || n != N || qq != Q) return false;
     if constexpr (FwdShape<IO, P, N, Q>::kFits) {
         if (launch) {
-            const long long blocks = max_entries * prm.G * prm.slices;
+            long long blocks = max_entries * prm.G * prm.slices;
+            blocks = (blocks + prm.n_xcd - 1) / prm.n_xcd * prm.n_xcd;
             hipLaunchKernelGGL((ssd_fwd_kernel<IO, P, N, Q>), dim3((unsigned)blocks),
                                dim3(FwdShape<IO, P, N, Q>::kThreads), 0, st, prm);
             *err = hipGetLastError();
