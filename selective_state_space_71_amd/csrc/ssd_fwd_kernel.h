@@ -325,11 +325,14 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         load_c(hasA ? Ia : S::QT, cga);
         load_c(hasB ? Ib : S::QT, cgb);
         __syncthreads();  // B chunk in LDS
-        f32x4 gtile[S::GT];
+        // Kept in the io precision (the decay-weighted mask built from it is
+        // rounded to the io type for the MFMA anyway); fp32 accumulation.
+        Half gtile[S::GT];
     #pragma unroll
         for (int J = 0; J < S::GT; ++J) {
             // (Ia, J) for J <= Ia, else (Ib, GT-1-J) for GT-1-J <= Ib
-            gtile[J] = zero4();
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) gtile[J][r] = from_f32<IO>(0.f);
             const bool useA = J <= Ia;
             const int jt = useA ? J : S::GT - 1 - J;
             const bool live = useA ? hasA : (hasB && jt <= Ib);
@@ -340,7 +343,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     const Frag bfr = *reinterpret_cast<const Frag *>(sB + (16 * jt + li) * S::SB + ks * 32 + 8 * lg);
                     acc = Io<IO>::mfma(acc, bfr, useA ? cga[ks] : cgb[ks]);
                 }
-                gtile[J] = acc;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) gtile[J][r] = from_f32<IO>(acc[r]);
             }
         }
 
@@ -364,7 +368,10 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 for (int half = 0; half < 2; ++half) {
                     const int jt = 2 * kj + half;
                     const int j0 = 32 * kj + 16 * half + 4 * lg;
-                    const f32x4 &gv = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
+                    const Half &gh = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
+                    f32x4 gv;
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) gv[r] = to_f32(gh[r]);
                     if (jt < I) {
                         const float rowf = exp2f_fast(s2_i - vRef[jt]);
                         const f32x4 col = *reinterpret_cast<const f32x4 *>(vCol + j0);
@@ -396,21 +403,38 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             f32x4 accO[S::PT];
     #pragma unroll
             for (int pt = 0; pt < S::PT; ++pt) accO[pt] = zero4();
+            // software pipeline: the H fragments of K step ks+1 are read while the
+            // MFMAs of step ks run (the scheduling barriers keep that order)
+            Frag hf[2][S::PT];
+            auto load_h = [&](int ks, Frag (&o)[S::PT]) {
     #pragma unroll
-            for (int ks = 0; ks < S::NK; ++ks)
+                for (int pt = 0; pt < S::PT; ++pt)
+                    o[pt] = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
+            };
+            load_h(0, hf[0]);
     #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt) {
-                    const Frag hf = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
-                    accO[pt] = Io<IO>::mfma(accO[pt], hf, cf[ks]);
-                }
+            for (int ks = 0; ks < S::NK; ++ks) {
+                if (ks + 1 < S::NK) load_h(ks + 1, hf[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt) accO[pt] = Io<IO>::mfma(accO[pt], hf[ks & 1][pt], cf[ks]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (i_row < q) {
                 const float eo = vEo[i_row];
+                float xv[S::PT][4];   // x[i_row][pt*16 + 4 lg + r], all read before use
+                const int xp = xpos(i_row);
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt)
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) xv[pt][r] = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + xp]);
+                __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
                 for (int pt = 0; pt < S::PT; ++pt) {
                     Half yv;
     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float xval = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + xpos(i_row)]);
+                        const float xval = xv[pt][r];
                         yv[r] = from_f32<IO>(accY[pt][r] + eo * accO[pt][r] + Dh * xval);
                     }
                     *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
@@ -425,6 +449,16 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             // Lane indices are made opaque per head so that per-head addresses
             // and predicates are recomputed rather than kept live across heads.
             asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(lg));
+            // (and so are the stored C B^T tiles, so that their conversion to
+            // fp32 is done at use instead of being hoisted out of the loop)
+    #pragma unroll
+            for (int J = 0; J < S::GT; ++J) {
+                if constexpr (sizeof(IO) == 2) {
+                    long long gbits = __builtin_bit_cast(long long, gtile[J]);
+                    asm volatile("" : "+v"(gbits));
+                    gtile[J] = __builtin_bit_cast(Half, gbits);
+                }
+            }
             IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
             const int unit = seq * H + h;
 
