@@ -353,16 +353,33 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
 
         // Diagonal block of tile I (transposed, Y^T = x^T M^T): accumulator
         // element r of tile pt is Y_diag[16 I + li][pt*16 + 4*lg + r].  `fromA`
-        // selects which end of gtile holds the tile's C B^T row.
-        auto diag_block = [&](auto from_a, int I, f32x4 (&accY)[S::PT]) {
+        // selects which end of gtile holds the tile's C B^T row.  The LDS
+        // operands of K step kj+1 are read before step kj's arithmetic (the
+        // scheduling barriers keep that order); sref holds the 16-tile
+        // reference cumsums in scalar registers.
+        auto diag_block = [&](auto from_a, int I, f32x4 (&accY)[S::PT], const float (&sref)[S::QT]) {
             constexpr bool fromA = decltype(from_a)::value;
             const int i_row = 16 * I + li;
             const float s2_i = vS2[i_row];
     #pragma unroll
             for (int pt = 0; pt < S::PT; ++pt) accY[pt] = zero4();
+            Frag xf[2][S::PT];
+            f32x4 colv[2][2];
+            auto load_step = [&](int kj, Frag (&xo)[S::PT], f32x4 (&co)[2]) {
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt)
+                    xo[pt] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + 32 * kj + 8 * lg);
+    #pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    co[half] = *reinterpret_cast<const f32x4 *>(vCol + 32 * kj + 16 * half + 4 * lg);
+            };
+            load_step(0, xf[0], colv[0]);
     #pragma unroll
             for (int kj = 0; kj < S::QT / 2; ++kj) {
                 if (kj > I / 2) break;
+                const int cur = kj & 1;
+                if (kj + 1 < S::QT / 2 && kj + 1 <= I / 2) load_step(kj + 1, xf[cur ^ 1], colv[cur ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
                 Frag m;  // lane holds M[i_row][j], j = 32 kj + 16 half + 4 lg + r
     #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -373,10 +390,9 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     #pragma unroll
                     for (int r = 0; r < 4; ++r) gv[r] = to_f32(gh[r]);
                     if (jt < I) {
-                        const float rowf = exp2f_fast(s2_i - vRef[jt]);
-                        const f32x4 col = *reinterpret_cast<const f32x4 *>(vCol + j0);
+                        const float rowf = exp2f_fast(s2_i - sref[jt]);
     #pragma unroll
-                        for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * col[r]);
+                        for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * colv[cur][half][r]);
                     } else if (jt == I) {
                         const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
                         const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
@@ -391,10 +407,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     }
                 }
     #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt) {
-                    const Frag xf = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + 32 * kj + 8 * lg);
-                    accY[pt] = Io<IO>::mfma(accY[pt], xf, m);
-                }
+                for (int pt = 0; pt < S::PT; ++pt) accY[pt] = Io<IO>::mfma(accY[pt], xf[cur][pt], m);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         // State read-out (H C^T) and the final combination of tile I.
@@ -580,8 +594,12 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 }
             }
             f32x4 accYa[S::PT], accYb[S::PT];
-            if (hasA) diag_block(std::true_type{}, Ia, accYa);
-            if (hasB) diag_block(std::false_type{}, Ib, accYb);
+            float sref[S::QT];   // 16-tile reference cumsums, wave-uniform
+    #pragma unroll
+            for (int t = 0; t < S::QT; ++t)
+                sref[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, vRef[t])));
+            if (hasA) diag_block(std::true_type{}, Ia, accYa, sref);
+            if (hasB) diag_block(std::false_type{}, Ib, accYb, sref);
 
             Frag cfa[S::NK];
             if (hasA) load_c(Ia, cfa);
