@@ -567,30 +567,50 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     #pragma unroll
                 for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
             if (wp < S::PT) {
-    #pragma unroll 2
-                for (int ks = 0; ks < S::QK; ++ks) {
-                    const f32x4 wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 4 * lg);
-                    const f32x4 whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 16 + 4 * lg);
+                // software pipeline: the operands of K step ks+1 are read while
+                // step ks is scaled and multiplied
+                struct ScOps {
+                    f32x4 wlo, whi;
                     Frag xf[S::PTW];
+                    Frag bt[S::NTW];
+                };
+                auto load_sc = [&](int ks, ScOps &o) {
+                    o.wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 4 * lg);
+                    o.whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 16 + 4 * lg);
     #pragma unroll
                     for (int b = 0; b < S::PTW; ++b) {
                         const int pt = wp + b * S::WP;
-                        xf[b] = zero_frag<Frag>();
+                        o.xf[b] = zero_frag<Frag>();
                         if (pt < S::PT)
-                            xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                            o.xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
                     }
     #pragma unroll
                     for (int a = 0; a < S::NTW; ++a) {
                         const int nt = wn + a * S::WN;
+                        o.bt[a] = zero_frag<Frag>();
+                        if (nt < S::NT) o.bt[a] = load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg);
+                    }
+                };
+                ScOps ops[2];
+                load_sc(0, ops[0]);
+    #pragma unroll
+                for (int ks = 0; ks < S::QK; ++ks) {
+                    const int cur = ks & 1;
+                    if (ks + 1 < S::QK) load_sc(ks + 1, ops[cur ^ 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int a = 0; a < S::NTW; ++a) {
+                        const int nt = wn + a * S::WN;
                         if (nt < S::NT) {
-                            const Frag bt = scale_frag<IO>(load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg), wlo, whi);
+                            const Frag bt = scale_frag<IO>(ops[cur].bt[a], ops[cur].wlo, ops[cur].whi);
     #pragma unroll
                             for (int b = 0; b < S::PTW; ++b) {
                                 const int pt = wp + b * S::WP;
-                                if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, xf[b]);
+                                if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, ops[cur].xf[b]);
                             }
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             f32x4 accYa[S::PT], accYb[S::PT];
