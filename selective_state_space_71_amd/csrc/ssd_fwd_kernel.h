@@ -44,6 +44,7 @@
 // Accumulation and the boundary state are fp32.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "ssd_device.h"
@@ -102,8 +103,8 @@ struct FwdShape {
     static constexpr int kLdsB = Q * SB * E;
     static constexpr int kLdsX = P * SX * E;
     static constexpr int kLdsH = P * SH * E;
-    static constexpr int kNVec = 6;              // per-token float vectors
-    static constexpr int kLdsVec = kNVec * Q * 4;
+    static constexpr int kNVec = 7;              // per-token float vectors (+ dt/A staging)
+    static constexpr int kLdsVec = kNVec * Q * 4 + 16;
     static constexpr int kLds = kLdsB + kLdsX + kLdsH + kLdsVec + 16;
     static constexpr bool kFits = kLds <= 160 * 1024 && QT <= 2 * kWaves;
 };
@@ -113,6 +114,27 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2f_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// v + (value of v in the lane selected by the DPP control `ctrl`), where lanes
+// without a source (or outside `row_mask`) add 0.
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask, 0xF, true);
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: four
+// shifts inside each 16-lane row, then row 0 and 2's last lane into rows 1
+// and 3, then lane 31 into rows 2 and 3.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+    v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+    v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+    v = dpp_add<0x118, 0xF>(v);   // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31
+    return v;
+}
 
 // K-slot order.  Every contraction over chunk tokens uses the same slot
 // order: within a 32-token K step, slot e (0..7) of lane group lg holds token
@@ -168,6 +190,7 @@ struct Prefetch {
     static constexpr int R = Q / 64;
     Frag x[NU][4];
     float dt[R];
+    float a;   // A[h] (wave 0)
 
     // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  Sixteen
     // consecutive units take sixteen consecutive token groups of one channel
@@ -196,7 +219,15 @@ struct Prefetch {
                 const int i = tid * R + k;
                 dt[k] = (i < q) ? prm.dt[(tok0 + i) * prm.H + h] : 0.f;
             }
+            a = prm.A[h];
         }
+    }
+
+    // wave 0: dt (lane holds tokens R*lane .. R*lane+R-1) and A into LDS
+    __device__ __forceinline__ void stage_dt(float *sStage, int lane) const {
+#pragma unroll
+        for (int k = 0; k < R; ++k) sStage[lane * R + k] = dt[k];
+        if (lane == 0) sStage[Q] = a;
     }
 
     // x^T[p][i .. i+3] from 4 tokens of one channel
@@ -238,7 +269,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     float *vW = vCol + Q;     // exp(s_last - s_j) dt_j
     float *vEo = vW + Q;      // exp(s_i)
     float *vRef = vEo + Q;    // s2 of the last token of each 16-tile (QT used)
-    int *sTicket = reinterpret_cast<int *>(vRef + Q);
+    float *sStage = vRef + Q; // next head's dt (Q values) and A, staged by wave 0
+    int *sTicket = reinterpret_cast<int *>(sStage + Q + 4);
 
     int tid = threadIdx.x;
     int lane = tid & 63;
@@ -324,7 +356,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         Frag cga[S::NK], cgb[S::NK];
         load_c(hasA ? Ia : S::QT, cga);
         load_c(hasB ? Ib : S::QT, cgb);
-        __syncthreads();  // B chunk in LDS
+        if (wave == 0) pf.stage_dt(sStage, lane);
+        __syncthreads();  // B chunk and the first head's dt in LDS
         // Kept in the io precision (the decay-weighted mask built from it is
         // rounded to the io type for the MFMA anyway); fp32 accumulation.
         Half gtile[S::GT];
@@ -476,48 +509,52 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
             const int unit = seq * H + h;
 
-            // ---- (1) stage x^T; wave 0: in-chunk cumulative sum and per-token vectors ----
+            // ---- (1) stage x^T; in-chunk cumulative sum and per-token vectors ----
             pf.stage(sX, tid);
-            if (wave == 0) {
+            {
+                // one early look at the predecessor's flag (the state loads can
+                // then be issued before the compute phase)
+                // (compared only after the scan, so that the scan does not wait for it)
+                int flagv = INT_MAX;
+                if (wave == 0 && lane == 0 && cloc > 0)
+                    flagv = __hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // Every wave scans the whole chunk (R tokens per lane, from the
+                // staged dt) and writes the per-token vectors of its own Q/8
+                // tokens (lanes 8 wave .. 8 wave + 7).
                 constexpr int R = Q / 64;
-                const float Ah = prm.A[h];   // read by the scan only
-                // one early look at the predecessor's flag (the state loads can then
-                // be issued before the compute phase)
-                int ready = 1;
-                if (cloc > 0 && lane == 0)
-                    ready = __hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S::kWaves * cloc;
+                const float Ah = sStage[Q];
+                float dtv[R];
+    #pragma unroll
+                for (int k = 0; k < R; ++k) dtv[k] = sStage[lane * R + k];
                 float s2[R];
                 float run = 0.f;
     #pragma unroll
                 for (int k = 0; k < R; ++k) {
-                    run += pf.dt[k] * Ah;
+                    run += dtv[k] * Ah;
                     s2[k] = run;
                 }
-                float incl = run;
-    #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float v = __shfl_up(incl, off, 64);
-                    if (lane >= off) incl += v;
-                }
-                const float excl = incl - run;
+                const float excl = wave_inclusive_sum(run) - run;
     #pragma unroll
                 for (int k = 0; k < R; ++k) s2[k] = (excl + s2[k]) * kLog2e;
-                const float s2_end = __shfl(s2[R - 1], 63, 64);
+                const float s2_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s2[R - 1]), 63));
                 // last token of each 16-token tile: index (i | 15), held by lane ((i | 15) / R)
                 const int ref_lane = ((lane * R) | 15) / R;
                 const float ref = __shfl(s2[R - 1], ref_lane, 64);
+                if ((lane >> 3) == wave) {
     #pragma unroll
-                for (int k = 0; k < R; ++k) {
-                    const int i = lane * R + k;
-                    const float d = pf.dt[k];
-                    vS2[i] = s2[k];
-                    vDt[i] = d;
-                    vCol[i] = exp2f_fast(ref - s2[k]) * d;
-                    vW[i] = exp2f_fast(s2_end - s2[k]) * d;
-                    vEo[i] = exp2f_fast(s2[k]);
-                    if ((i & 15) == 15) vRef[i >> 4] = s2[k];
+                    for (int k = 0; k < R; ++k) {
+                        const int i = lane * R + k;
+                        const float d = dtv[k];
+                        vS2[i] = s2[k];
+                        vDt[i] = d;
+                        vCol[i] = exp2f_fast(ref - s2[k]) * d;
+                        vW[i] = exp2f_fast(s2_end - s2[k]) * d;
+                        vEo[i] = exp2f_fast(s2[k]);
+                        if ((i & 15) == 15) vRef[i >> 4] = s2[k];
+                    }
                 }
-                if (lane == 0) *sReady = ready;
+                asm volatile("" : "+v"(flagv));   // keeps the comparison (and its wait) here
+                if (wave == 0 && lane == 0) *sReady = flagv >= S::kWaves * cloc;
             }
             if constexpr (S::NP != N) {
                 for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
@@ -679,6 +716,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
             if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (hasB) finish_tile(Ib, cfb, accYb, yg, Dh);
+            if (wave == 0 && h + 1 < h_end) pf.stage_dt(sStage, lane);   // the next head's dt and A
             __syncthreads();  // every wave is done with this head's LDS tiles
         }
     }
