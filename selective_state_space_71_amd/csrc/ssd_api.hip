@@ -116,12 +116,37 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
         build_packed_schedule(p);
     }
     __syncthreads();
-    // per-XCD item lists: counts, offsets, then an order-preserving placement
+    // per-XCD item lists: counts, offsets, then an order-preserving placement.
+    // The sequence of each entry is cached in LDS (the placement loop would
+    // otherwise wait on one global load per step).
+    constexpr int kSeqCache = 4096;
+    __shared__ int sseq[kSeqCache];
+    const int n_entries = *p.n_chunks;
+    const bool dense = p.cu_seqlens == nullptr;
+    for (int e = tid; e < n_entries && e < kSeqCache; e += 256) sseq[e] = dense ? e % p.batch : p.chunks[e].x;
+    __syncthreads();
     const int GS = p.G * p.slices;
-    const int n_items = *p.n_chunks * GS;
+    const int n_items = n_entries * GS;
+    if (GS % p.n_xcd == 0) {
+        // item j of every entry goes to XCD j mod n_xcd (the sequence term is
+        // a multiple of n_xcd): the lists have a closed form, written in parallel
+        const int per = GS / p.n_xcd;
+        if (tid < 16) {
+            p.xcd_count[tid] = tid < p.n_xcd ? n_entries * per : 0;
+            p.xcd_offset[tid] = (tid < p.n_xcd ? tid : p.n_xcd) * n_entries * per;
+        }
+        for (int i = tid; i < n_items; i += 256) {
+            const int e = i / GS;
+            const int j = i - e * GS;
+            const int x = j % p.n_xcd;
+            p.items[x * n_entries * per + e * per + j / p.n_xcd] = i;
+        }
+        return;
+    }
     auto xcd_of = [&](int i) {
         const int e = i / GS;
-        return (p.chunks[e].x * GS + (i - e * GS)) % p.n_xcd;
+        const int seq = e < kSeqCache ? sseq[e] : p.chunks[e].x;
+        return (seq * GS + (i - e * GS)) % p.n_xcd;
     };
     for (int i = tid; i < n_items; i += 256) atomicAdd(&cnt[xcd_of(i)], 1);
     __syncthreads();
