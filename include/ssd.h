@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
     SSD_OK = 0,
@@ -72,6 +72,26 @@ typedef struct {
     int32_t ngroups;  /* G, groups sharing B and C; nheads % ngroups == 0            */
     int32_t nseq;     /* number of sequences: == batch when cu_seqlens is NULL       */
 } ssd_dims_t;
+
+/*
+ * Optional step-size preprocessing, applied on the device before dt is used.
+ * The selective step size of the "20.1 상태 공간 모델 (SSM)" textbook chapter,
+ * section 2, is the softplus of a linear projection of the input; dt_bias is
+ * that projection's bias, one value per head.  Per token t and head h:
+ *     v  = dt[t, h] + (dt_bias ? dt_bias[h] : 0)
+ *     v  = softplus ? log(1 + exp(v)) : v
+ *     dt = min(max(v, dt_min), dt_max)
+ * (tokens beyond a sequence's end are not touched).  A NULL options pointer
+ * uses dt as given.  dt_min <= dt_max is required (NaN bounds are rejected);
+ * -INFINITY and INFINITY disable the clamp.
+ *   dt_bias   [nheads] fp32 device pointer, or NULL
+ */
+typedef struct {
+    const float *dt_bias;
+    int32_t softplus;   /* nonzero: apply the softplus                          */
+    float dt_min;       /* lower clamp after the softplus                       */
+    float dt_max;       /* upper clamp after the softplus                       */
+} ssd_dt_opts_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *ssd_status_string(ssd_status_t status);
@@ -136,6 +156,19 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssd_chunk_scan_fwd with step-size preprocessing (see ssd_dt_opts_t): `dt`
+ * then holds the raw projection output.  dt_opts may be NULL (identical to
+ * ssd_chunk_scan_fwd).  dt_bias must not overlap y or final_state.
+ */
+ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
+                                   int32_t chunk_len, const ssd_dt_opts_t *dt_opts,
+                                   const void *x, const float *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   const float *init_state, const int32_t *cu_seqlens,
+                                   void *y, float *final_state,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Reads the device-side failure word of a workspace after a forward call
  * (synchronises `stream`).  Returns SSD_OK, or SSD_ERR_DEVICE when a chunk
  * waited too long for its predecessor's state (the outputs of that call are
@@ -164,6 +197,16 @@ ssd_status_t ssd_decode_step(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
                              float *state, const void *x, const float *dt,
                              const float *A, const void *B, const void *C,
                              const float *D, void *y, void *stream);
+
+/*
+ * ssd_decode_step with step-size preprocessing (see ssd_dt_opts_t); dt_opts
+ * may be NULL.  dt_bias must not overlap y or state.
+ */
+ssd_status_t ssd_decode_step_ex(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
+                                const ssd_dt_opts_t *dt_opts, float *state,
+                                const void *x, const float *dt, const float *A,
+                                const void *B, const void *C, const float *D,
+                                void *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -129,3 +129,21 @@ def ssd_decode(state, x, dt, A, B, C, D=None, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_decode failed with code {rc}")
     return y, st
+
+
+def dt_preprocess(dt_raw, dt_bias=None, softplus: bool = False, dt_min: float = -np.inf,
+                  dt_max: float = np.inf):
+    """Step-size preprocessing in fp64: clamp(softplus(dt_raw + dt_bias)).
+
+    The "20.1 상태 공간 모델 (SSM)" textbook chapter, section 2, makes the step
+    size the softplus of a linear projection of the input; dt_bias is that
+    projection's bias, one value per head (the last axis of dt_raw).  The clamp
+    bounds are applied after the softplus.  softplus(v) = log(1 + exp(v)) is
+    evaluated as max(v, 0) + log1p(exp(-|v|)), which does not overflow.
+    """
+    v = np.asarray(dt_raw, dtype=np.float64)
+    if dt_bias is not None:
+        v = v + np.asarray(dt_bias, dtype=np.float64)
+    if softplus:
+        v = np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))
+    return np.minimum(np.maximum(v, dt_min), dt_max)

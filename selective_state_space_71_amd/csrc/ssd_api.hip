@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 
@@ -192,6 +193,7 @@ struct DecodeParams {
     float *state;
     const void *x;
     const float *dt;
+    DtProc dtp;
     const float *A;
     const void *B;
     const void *C;
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void ssd_decode_kernel(DecodeParams p) {
     float bv[4], cv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) { bv[k] = to_f32(Bp[k]); cv[k] = to_f32(Cp[k]); }
-    const float d = p.dt[u];
+    const float d = p.dtp.on ? p.dtp.apply(p.dt[u], p.dtp.bias ? p.dtp.bias[h] : 0.f) : p.dt[u];
     const float abar = __expf(d * p.A[h]);
     const float Dh = p.D ? p.D[h] : 0.f;
     const IO *xp = reinterpret_cast<const IO *>(p.x) + (long long)u * p.P;
@@ -344,6 +346,20 @@ bool dims_ok(const ssd_dims_t &d) {
            d.ngroups >= 1 && d.nseq >= 1 && d.nheads % d.ngroups == 0;
 }
 
+// Validates the step-size options and fills the kernels' view of them.
+ssd_status_t dt_opts_check(const ssd_dt_opts_t *o, const ssd_dims_t &d, ssd::DtProc *out) {
+    (void)d;
+    *out = ssd::DtProc{};
+    if (!o) return SSD_OK;
+    if (!(o->dt_min <= o->dt_max)) return SSD_ERR_SHAPE;   // also rejects NaN bounds
+    out->bias = o->dt_bias;
+    out->softplus = o->softplus != 0;
+    out->lo = o->dt_min;
+    out->hi = o->dt_max;
+    out->on = o->dt_bias != nullptr || o->softplus != 0 || o->dt_min > -INFINITY || o->dt_max < INFINITY;
+    return SSD_OK;
+}
+
 ssd_status_t fwd_shape_check(const ssd_dims_t *dims, int32_t chunk_len, ssd_dtype_t io, bool varlen) {
     if (!dims) return SSD_ERR_NULL_PTR;
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
@@ -407,13 +423,26 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
                                 const void *C, const float *D, const float *init_state,
                                 const int32_t *cu_seqlens, void *y, float *final_state,
                                 void *workspace, size_t workspace_bytes, void *stream) {
+    return ssd_chunk_scan_fwd_ex(dims, io, chunk_len, nullptr, x, dt, A, B, C, D, init_state, cu_seqlens, y,
+                                 final_state, workspace, workspace_bytes, stream);
+}
+
+ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
+                                   const ssd_dt_opts_t *dt_opts, const void *x, const float *dt,
+                                   const float *A, const void *B, const void *C, const float *D,
+                                   const float *init_state, const int32_t *cu_seqlens, void *y,
+                                   float *final_state, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
     const bool varlen = cu_seqlens != nullptr;
     ssd_status_t st = fwd_shape_check(dims, chunk_len, io, varlen);
+    if (st != SSD_OK) return st;
+    ssd::DtProc dtp{};
+    st = dt_opts_check(dt_opts, *dims, &dtp);
     if (st != SSD_OK) return st;
     const ssd_dims_t &d = *dims;
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_PTR;
     if (!workspace) return SSD_ERR_WORKSPACE;
-    const void *al16[] = {x, dt, A, B, C, D, init_state, y, final_state};
+    const void *al16[] = {x, dt, A, B, C, D, init_state, y, final_state, dtp.bias};
     for (const void *p : al16)
         if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
     if (!aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
@@ -429,6 +458,8 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
     const Range rB = rng(B, nbc), rC = rng(C, nbc), rD = rng(D, D ? (size_t)d.nheads * 4 : 0);
     const Range ri = rng(init_state, init_state ? nstate : 0), rf = rng(final_state, final_state ? nstate : 0);
     const Range rcu = rng(cu_seqlens, cu_seqlens ? (size_t)(d.nseq + 1) * 4 : 0);
+    const Range rbias = rng(dtp.bias, dtp.bias ? (size_t)d.nheads * 4 : 0);
+    if (overlap(ry, rbias) || overlap(rf, rbias)) return SSD_ERR_ALIAS;
     WsLayout w{};
     ws_layout(d, chunk_len, varlen, &w);
     if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
@@ -482,6 +513,7 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
     ssd::FwdParams fp{};
     fp.x = x;
     fp.dt = dt;
+    fp.dtp = dtp;
     fp.A = A;
     fp.B = B;
     fp.C = C;
@@ -525,16 +557,25 @@ ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream) {
 ssd_status_t ssd_decode_step(const ssd_dims_t *dims, ssd_dtype_t io, float *state, const void *x,
                              const float *dt, const float *A, const void *B, const void *C,
                              const float *D, void *y, void *stream) {
+    return ssd_decode_step_ex(dims, io, nullptr, state, x, dt, A, B, C, D, y, stream);
+}
+
+ssd_status_t ssd_decode_step_ex(const ssd_dims_t *dims, ssd_dtype_t io, const ssd_dt_opts_t *dt_opts,
+                                float *state, const void *x, const float *dt, const float *A,
+                                const void *B, const void *C, const float *D, void *y, void *stream) {
     if (!dims) return SSD_ERR_NULL_PTR;
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
     const ssd_dims_t &d = *dims;
     if (d.batch < 1 || d.nheads < 1 || d.headdim < 1 || d.dstate < 1 || d.ngroups < 1 ||
         d.nheads % d.ngroups != 0)
         return SSD_ERR_SHAPE;
+    ssd::DtProc dtp{};
+    ssd_status_t st = dt_opts_check(dt_opts, d, &dtp);
+    if (st != SSD_OK) return st;
     const int N = d.dstate;
     if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return SSD_ERR_UNSUPPORTED;
     if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_PTR;
-    const void *al16[] = {state, x, dt, A, B, C, D, y};
+    const void *al16[] = {state, x, dt, A, B, C, D, y, dtp.bias};
     for (const void *p : al16)
         if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
     const size_t E = (io == SSD_BF16) ? 2 : 4;
@@ -549,10 +590,13 @@ ssd_status_t ssd_decode_step(const ssd_dims_t *dims, ssd_dtype_t io, float *stat
         if (overlap(ry, r)) return SSD_ERR_ALIAS;
     for (Range r : {rx, rdt, rA, rB, rC, rD})
         if (overlap(rs, r)) return SSD_ERR_ALIAS;
+    const Range rbias = rng(dtp.bias, dtp.bias ? (size_t)d.nheads * 4 : 0);
+    if (overlap(ry, rbias) || overlap(rs, rbias)) return SSD_ERR_ALIAS;
     ssd::DecodeParams p{};
     p.state = state;
     p.x = x;
     p.dt = dt;
+    p.dtp = dtp;
     p.A = A;
     p.B = B;
     p.C = C;

@@ -71,4 +71,17 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16 *p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// Step-size preprocessing (see ssd_dt_opts_t): dt = clamp(softplus(dt + bias)).
+struct DtProc {
+    const float *bias;   // [nheads] or null
+    bool on;             // any preprocessing at all
+    bool softplus;
+    float lo, hi;
+    __device__ __forceinline__ float apply(float v, float b) const {
+        v += b;
+        if (softplus) v = v > 20.f ? v : log1pf(expf(v));
+        return fminf(fmaxf(v, lo), hi);
+    }
+};
+
 }  // namespace ssd

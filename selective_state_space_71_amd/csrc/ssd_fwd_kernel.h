@@ -54,6 +54,7 @@ namespace ssd {
 struct FwdParams {
     const void *x;
     const float *dt;
+    DtProc dtp;               // optional step-size preprocessing
     const float *A;
     const void *B;
     const void *C;
@@ -191,6 +192,7 @@ struct Prefetch {
     Frag x[NU][4];
     float dt[R];
     float a;   // A[h] (wave 0)
+    float braw; // dt_bias[h] (A[h] when there is no bias; not used then)
 
     // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  Sixteen
     // consecutive units take sixteen consecutive token groups of one channel
@@ -220,13 +222,19 @@ struct Prefetch {
                 dt[k] = (i < q) ? prm.dt[(tok0 + i) * prm.H + h] : 0.f;
             }
             a = prm.A[h];
+            braw = (prm.dtp.bias ? prm.dtp.bias : prm.A)[h];   // branch-free
         }
     }
 
-    // wave 0: dt (lane holds tokens R*lane .. R*lane+R-1) and A into LDS
-    __device__ __forceinline__ void stage_dt(float *sStage, int lane) const {
+    // wave 0: dt (lane holds tokens R*lane .. R*lane+R-1, preprocessed when
+    // asked; tokens past the chunk stay 0) and A into LDS
+    __device__ __forceinline__ void stage_dt(float *sStage, int lane, int q, const DtProc &dtp) const {
 #pragma unroll
-        for (int k = 0; k < R; ++k) sStage[lane * R + k] = dt[k];
+        for (int k = 0; k < R; ++k) {
+            float v = dt[k];
+            if (dtp.on && lane * R + k < q) v = dtp.apply(v, dtp.bias ? braw : 0.f);
+            sStage[lane * R + k] = v;
+        }
         if (lane == 0) sStage[Q] = a;
     }
 
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         Frag cga[S::NK], cgb[S::NK];
         load_c(hasA ? Ia : S::QT, cga);
         load_c(hasB ? Ib : S::QT, cgb);
-        if (wave == 0) pf.stage_dt(sStage, lane);
+        if (wave == 0) pf.stage_dt(sStage, lane, q, prm.dtp);
         __syncthreads();  // B chunk and the first head's dt in LDS
         // Kept in the io precision (the decay-weighted mask built from it is
         // rounded to the io type for the MFMA anyway); fp32 accumulation.
@@ -716,7 +724,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
             if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (hasB) finish_tile(Ib, cfb, accYb, yg, Dh);
-            if (wave == 0 && h + 1 < h_end) pf.stage_dt(sStage, lane);   // the next head's dt and A
+            if (wave == 0 && h + 1 < h_end) pf.stage_dt(sStage, lane, q, prm.dtp);   // the next head's dt and A
             __syncthreads();  // every wave is done with this head's LDS tiles
         }
     }

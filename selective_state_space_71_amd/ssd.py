@@ -8,6 +8,9 @@ cannot be loaded), every call raises -- there is no fallback path.
                                     init_state=None, cu_seqlens=None)
     y = decode_step(state, x, dt, A, B, C, D=None)      # updates state in place
 
+Both take optional step-size preprocessing (dt_bias=[nheads] fp32,
+dt_softplus=bool, dt_limit=(lo, hi)): dt = clamp(softplus(dt + dt_bias)).
+
 Shapes (row-major, contiguous):
     x, y        [batch, seqlen, nheads, headdim]   bf16 or fp32 ("io" dtype)
     dt          [batch, seqlen, nheads]            fp32 (final positive step)
@@ -47,6 +50,11 @@ class SsdDims(ctypes.Structure):
                 ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "nseq")]
 
 
+class SsdDtOpts(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("softplus", ctypes.c_int32),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+
+
 _lib = None
 _VP = ctypes.c_void_p
 
@@ -72,6 +80,17 @@ def load_library(path: str = LIB_PATH):
         ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.c_int32,
         _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
         _VP, ctypes.c_size_t, _VP,
+    ]
+    lib.ssd_chunk_scan_fwd_ex.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_ex.argtypes = [
+        ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.c_int32, ctypes.POINTER(SsdDtOpts),
+        _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+        _VP, ctypes.c_size_t, _VP,
+    ]
+    lib.ssd_decode_step_ex.restype = ctypes.c_int
+    lib.ssd_decode_step_ex.argtypes = [
+        ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.POINTER(SsdDtOpts),
+        _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
     ]
     lib.ssd_chunk_scan_fwd_check.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_check.argtypes = [_VP, _VP]
@@ -122,6 +141,16 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _dt_opts(dt_bias, dt_softplus, dt_limit, H, dev):
+    """ssd_dt_opts_t for the given preprocessing, or None when there is none."""
+    if dt_bias is None and not dt_softplus and dt_limit is None:
+        return None
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    lo, hi = dt_limit if dt_limit is not None else (-float("inf"), float("inf"))
+    return SsdDtOpts(None if dt_bias is None else dt_bias.data_ptr(), 1 if dt_softplus else 0, lo, hi)
+
+
 def fwd_dims(x, B, cu_seqlens=None) -> SsdDims:
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -135,8 +164,8 @@ def workspace_size(dims: SsdDims, chunk_len: int, io: int) -> int:
 
 def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None,
                    cu_seqlens=None, return_final_state: bool = True, y=None, final_state=None,
-                   workspace=None):
-    """SSD forward through ``ssd_chunk_scan_fwd``.  Returns (y, final_state)."""
+                   workspace=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None):
+    """SSD forward through ``ssd_chunk_scan_fwd_ex``.  Returns (y, final_state)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", device=dev)
@@ -174,13 +203,14 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None
         raise SsdError(code, "ssd_chunk_scan_fwd (size query)")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    code = lib.ssd_chunk_scan_fwd(
-        ctypes.byref(dims), io, int(chunk_len),
+    opts = _dt_opts(dt_bias, dt_softplus, dt_limit, H, dev)
+    code = lib.ssd_chunk_scan_fwd_ex(
+        ctypes.byref(dims), io, int(chunk_len), None if opts is None else ctypes.byref(opts),
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
         _ptr(cu_seqlens), _ptr(y), _ptr(final_state),
         _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev))
     if code != 0:
-        raise SsdError(code, "ssd_chunk_scan_fwd")
+        raise SsdError(code, "ssd_chunk_scan_fwd_ex")
     chunk_scan_fwd.last_workspace = workspace
     return y, final_state
 
@@ -192,8 +222,9 @@ def check_workspace(workspace, device=None) -> int:
     return int(lib.ssd_chunk_scan_fwd_check(_ptr(workspace), _stream(dev)))
 
 
-def decode_step(state, x, dt, A, B, C, D=None, y=None):
-    """One decode step through ``ssd_decode_step``; ``state`` is updated in place."""
+def decode_step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool = False,
+                dt_limit=None):
+    """One decode step through ``ssd_decode_step_ex``; ``state`` is updated in place."""
     lib = load_library()
     dev = x.device
     _need(x, "x", device=dev)
@@ -210,8 +241,10 @@ def decode_step(state, x, dt, A, B, C, D=None, y=None):
     if y is None:
         y = torch.empty_like(x)
     dims = SsdDims(b, 1, H, P, N, G, b)
-    code = lib.ssd_decode_step(ctypes.byref(dims), io, _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
-                               _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
+    opts = _dt_opts(dt_bias, dt_softplus, dt_limit, H, dev)
+    code = lib.ssd_decode_step_ex(ctypes.byref(dims), io, None if opts is None else ctypes.byref(opts),
+                                  _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(y), _stream(dev))
     if code != 0:
-        raise SsdError(code, "ssd_decode_step")
+        raise SsdError(code, "ssd_decode_step_ex")
     return y

@@ -23,7 +23,8 @@ def lib():
 def test_header_symbols_are_exported(lib):
     names = ssd.header_functions()
     assert {"ssd_chunk_scan_fwd", "ssd_decode_step", "ssd_chunk_scan_fwd_workspace_size",
-            "ssd_status_string", "ssd_abi_version", "ssd_chunk_scan_fwd_check"} <= set(names)
+            "ssd_status_string", "ssd_abi_version", "ssd_chunk_scan_fwd_check",
+            "ssd_chunk_scan_fwd_ex", "ssd_decode_step_ex"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -33,7 +34,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 1
+    assert lib.ssd_abi_version() == 2
     for code, name in ssd._STATUS.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(77)
@@ -124,6 +125,32 @@ def _dec(lib, dims, io=ssd.SSD_BF16, **ptrs):
 def test_decode_validation_rejects(lib, case, expect):
     dims = case.pop("dims", _dims())
     assert _dec(lib, dims, **case) == expect
+
+
+def _opts(bias=None, softplus=1, lo=-float("inf"), hi=float("inf")):
+    return ssd.SsdDtOpts(bias, softplus, lo, hi)
+
+
+@pytest.mark.parametrize("opts,expect", [
+    (_opts(lo=1.0, hi=0.5), 2),                                  # dt_min > dt_max
+    (_opts(lo=float("nan")), 2),                                 # NaN bound
+    (_opts(bias=FAKE + (1 << 30) + 4), 5),                       # misaligned dt_bias
+    (_opts(bias=FAKE + (8 << 30) + 64), 6),                      # dt_bias overlaps y
+])
+def test_dt_options_validation(lib, opts, expect):
+    # forward: same fake pointers as _fwd, through the _ex entry point
+    dims = _dims()
+    rc = lib.ssd_chunk_scan_fwd_ex(ctypes.byref(dims), ssd.SSD_BF16, 256, ctypes.byref(opts), FAKE,
+                                   FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30),
+                                   None, None, None, FAKE + (8 << 30), None, FAKE + (16 << 30),
+                                   ctypes.c_size_t(1 << 40), None)
+    assert rc == expect
+    if expect == 6:
+        opts = _opts(bias=FAKE + (6 << 34) + 64)                 # overlaps the decode y
+    rc = lib.ssd_decode_step_ex(ctypes.byref(dims), ssd.SSD_BF16, ctypes.byref(opts), FAKE,
+                                FAKE + (1 << 34), FAKE + (2 << 34), FAKE + (3 << 34), FAKE + (4 << 34),
+                                FAKE + (5 << 34), None, FAKE + (6 << 34), None)
+    assert rc == expect
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -313,3 +313,37 @@ def test_varlen_lengths_recipe():
     rng = np.random.default_rng([71003, 1])
     lens = wl.varlen_lengths(rng, 16, 65536, 64, 8192)
     assert lens.sum() == 65536 and lens.min() >= 64 and lens.max() <= 8192 and len(lens) == 16
+
+
+# ------------------------------------------------- step-size preprocessing
+def test_dt_preprocess_softplus_pins():
+    """Softplus of the textbook chapter's section 2: closed forms and the exact
+    identity softplus(v) - softplus(-v) = v."""
+    v = np.linspace(-40.0, 40.0, 161)
+    sp = oracle.dt_preprocess(v, softplus=True)
+    assert abs(oracle.dt_preprocess(np.zeros(1), softplus=True)[0] - math.log(2.0)) < 1e-15
+    np.testing.assert_allclose(sp - oracle.dt_preprocess(-v, softplus=True), v, rtol=0, atol=1e-13)
+    assert np.all(sp > 0) and np.all(np.diff(sp) > 0)
+    # tails: exp(v) for very negative v, v for large v
+    np.testing.assert_allclose(oracle.dt_preprocess(np.array([-30.0]), softplus=True), [math.exp(-30.0)],
+                               rtol=1e-12)
+    np.testing.assert_allclose(oracle.dt_preprocess(np.array([30.0]), softplus=True), [30.0], rtol=1e-12)
+    # derivative is the logistic function (finite difference at a few points)
+    for x0 in (-3.0, 0.0, 2.5):
+        h = 1e-6
+        d = (oracle.dt_preprocess(np.array([x0 + h]), softplus=True)[0]
+             - oracle.dt_preprocess(np.array([x0 - h]), softplus=True)[0]) / (2 * h)
+        assert abs(d - 1.0 / (1.0 + math.exp(-x0))) < 1e-8
+
+
+def test_dt_preprocess_bias_per_head_and_clamp():
+    rng = np.random.default_rng(11)
+    raw = rng.normal(size=(2, 5, 3))
+    bias = np.array([-2.0, 0.0, 1.5])
+    out = oracle.dt_preprocess(raw, bias, softplus=False)
+    np.testing.assert_array_equal(out[..., 0], raw[..., 0] - 2.0)
+    np.testing.assert_array_equal(out[..., 2], raw[..., 2] + 1.5)
+    cl = oracle.dt_preprocess(raw, bias, softplus=True, dt_min=0.2, dt_max=0.9)
+    assert cl.min() >= 0.2 and cl.max() <= 0.9
+    inside = (cl > 0.2) & (cl < 0.9)
+    np.testing.assert_array_equal(cl[inside], oracle.dt_preprocess(raw, bias, softplus=True)[inside])
