@@ -142,9 +142,11 @@ size_t ssd_chunk_scan_fwd_workspace_size(const ssd_dims_t *dims, int32_t chunk_l
  *               aligned, not used by another call in flight.
  *   stream      hipStream_t, or NULL for the default stream.
  *
- * Supported sizes: headdim in {16, 32, 64}; dstate in {16, 32, 64, 128};
- * chunk_len in {64, 128, 256}; combinations whose chunk tiles do not fit in
- * the 160 KB of LDS of a gfx950 compute unit return SSD_ERR_UNSUPPORTED.
+ * Supported sizes: headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
+ * 256}; chunk_len in {64, 128, 256}; combinations whose chunk tiles do not
+ * fit in the 160 KB of LDS of a gfx950 compute unit return
+ * SSD_ERR_UNSUPPORTED (bf16: headdim 128 or dstate 256 need chunk_len <= 128,
+ * both together chunk_len 64; fp32 io needs smaller chunks still).
  * x, y, B, C, dt, D and the states must be 16-byte aligned.
  */
 ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,

@@ -41,12 +41,14 @@ static bool fwd_try_q(SSD_FWD_PARAMS) {
 template <typename IO, int P>
 static bool fwd_try_n(SSD_FWD_PARAMS) {
     return fwd_try_q<IO, P, 16>(SSD_FWD_ARGS) || fwd_try_q<IO, P, 32>(SSD_FWD_ARGS) ||
-           fwd_try_q<IO, P, 64>(SSD_FWD_ARGS) || fwd_try_q<IO, P, 128>(SSD_FWD_ARGS);
+           fwd_try_q<IO, P, 64>(SSD_FWD_ARGS) || fwd_try_q<IO, P, 128>(SSD_FWD_ARGS) ||
+           fwd_try_q<IO, P, 256>(SSD_FWD_ARGS);
 }
 
 template <typename IO>
 static bool fwd_dispatch(SSD_FWD_PARAMS) {
-    return fwd_try_n<IO, 16>(SSD_FWD_ARGS) || fwd_try_n<IO, 32>(SSD_FWD_ARGS) || fwd_try_n<IO, 64>(SSD_FWD_ARGS);
+    return fwd_try_n<IO, 16>(SSD_FWD_ARGS) || fwd_try_n<IO, 32>(SSD_FWD_ARGS) || fwd_try_n<IO, 64>(SSD_FWD_ARGS) ||
+           fwd_try_n<IO, 128>(SSD_FWD_ARGS);
 }
 
 }  // namespace ssd

@@ -70,6 +70,16 @@ def test_workspace_size_query(lib):
     assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=48)), 256, ssd.SSD_BF16) == 0
     assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims()), 128, ssd.SSD_F32) > 0
     assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=16, dstate=16)), 64, ssd.SSD_F32) > 0
+    # every head dim in {16, 32, 64, 128} and state dim in {16, ..., 256} is built
+    # at the chunk lengths whose tiles fit in LDS
+    for P in (16, 32, 64, 128):
+        for N in (16, 32, 64, 128, 256):
+            assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=P, dstate=N)), 64,
+                                                         ssd.SSD_BF16) > 0, (P, N)
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=128)), 128, ssd.SSD_BF16) > 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=64, dstate=256)), 128, ssd.SSD_BF16) > 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=256)), 128, ssd.SSD_BF16) == 0
+    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=256)), 64, ssd.SSD_F32) == 0
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -80,8 +90,9 @@ def test_workspace_size_query(lib):
     (dict(dims=_dims(nseq=3)), 2),                               # dense needs nseq == batch
     (dict(Q=100), 4),
     (dict(dims=_dims(headdim=48)), 4),
-    (dict(dims=_dims(dstate=256)), 4),
-    (dict(dims=_dims(headdim=128)), 4),                          # head dim not built
+    (dict(dims=_dims(dstate=256)), 4),                           # bf16 tiles exceed LDS at Q=256
+    (dict(dims=_dims(headdim=128)), 4),                          # likewise
+    (dict(dims=_dims(headdim=256)), 4),                          # head dim not built
     (dict(x=None), 1),
     (dict(A=None), 1),
     (dict(ws=None), 7),

@@ -61,6 +61,11 @@ def _check_fwd(inp, chunk_len, tol=None, tag=""):
     (1, 1000, 8, 64, 128, 4, 128, True),
     (3, 64, 2, 64, 32, 1, 64, True),
     (1, 1, 2, 64, 128, 1, 256, True),
+    # the larger head and state dims
+    (1, 300, 2, 128, 128, 1, 128, True),
+    (2, 200, 2, 64, 256, 1, 128, True),
+    (1, 150, 2, 128, 256, 1, 64, True),
+    (1, 520, 3, 128, 64, 1, 256, True),
 ])
 def test_bf16_small(shape):
     b, L, H, P, N, G, Q, init = shape
@@ -74,6 +79,10 @@ def test_bf16_small(shape):
     (2, 200, 2, 32, 32, 1, 128, True),
     (1, 190, 3, 16, 64, 1, 256, False),
     (1, 333, 4, 64, 16, 2, 64, True),
+    (1, 200, 2, 128, 64, 1, 64, True),
+    (1, 140, 2, 64, 256, 1, 64, False),
+    (1, 300, 2, 128, 128, 1, 64, True),
+    (1, 270, 2, 64, 64, 1, 256, True),
 ])
 def test_fp32_small(shape):
     b, L, H, P, N, G, Q, init = shape
