@@ -268,10 +268,13 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     static_assert(S::kFits, "chunk tiles do not fit in LDS");
 
     __shared__ __attribute__((aligned(16))) char smem[S::kLds];
-    IO *sB = reinterpret_cast<IO *>(smem);
-    IO *sX = reinterpret_cast<IO *>(smem + S::kLdsB);
-    IO *sH = reinterpret_cast<IO *>(smem + S::kLdsB + S::kLdsX);
-    float *vS2 = reinterpret_cast<float *>(smem + S::kLdsB + S::kLdsX + S::kLdsH);  // s * log2(e)
+    // The small per-token vectors and the x^T and state tiles come first, so
+    // that their addresses fit the 16-bit immediate offset of LDS instructions;
+    // the B chunk (the largest tile) is last.
+    float *vS2 = reinterpret_cast<float *>(smem);  // s * log2(e)
+    IO *sX = reinterpret_cast<IO *>(smem + S::kLdsVec + 16);
+    IO *sH = reinterpret_cast<IO *>(smem + S::kLdsVec + 16 + S::kLdsX);
+    IO *sB = reinterpret_cast<IO *>(smem + S::kLdsVec + 16 + S::kLdsX + S::kLdsH);
     float *vDt = vS2 + Q;     // dt_j
     float *vCol = vDt + Q;    // exp(s_r - s_j) dt_j, r = last token of j's 16-tile
     float *vW = vCol + Q;     // exp(s_last - s_j) dt_j
@@ -611,6 +614,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             for (int a = 0; a < S::NTW; ++a)
     #pragma unroll
                 for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
+            auto chunk_state = [&]() {
             if (wp < S::PT) {
                 // software pipeline: the operands of K step ks+1 are read while
                 // step ks is scaled and multiplied
@@ -658,6 +662,13 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            };
+            // The two waves that share a SIMD (w and w + kWaves/2) take the
+            // MFMA-dense chunk state and the VALU-dense diagonal blocks in
+            // opposite orders, so that one's matrix work overlaps the other's
+            // vector work.
+            const bool sc_first = wave < S::kWaves / 2;
+            if (sc_first) chunk_state();
             f32x4 accYa[S::PT], accYb[S::PT];
             float sref[S::QT];   // 16-tile reference cumsums, wave-uniform
     #pragma unroll
@@ -665,6 +676,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 sref[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, vRef[t])));
             if (hasA) diag_block(std::true_type{}, Ia, accYa, sref);
             if (hasB) diag_block(std::false_type{}, Ib, accYb, sref);
+            if (!sc_first) chunk_state();
 
             Frag cfa[S::NK];
             if (hasA) load_c(Ia, cfa);
