@@ -147,3 +147,84 @@ def dt_preprocess(dt_raw, dt_bias=None, softplus: bool = False, dt_min: float = 
     if softplus:
         v = np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))
     return np.minimum(np.maximum(v, dt_min), dt_max)
+
+
+# --------------------------------------------------------------------------
+# Block prologue and epilogue around the SSD layer.
+#
+# The Mamba block of the feghi.github.io Mamba review (section 5, the block
+# figure read bottom to top) sends one projected branch through a short causal
+# convolution and an activation before the selective SSM, while the other
+# branch becomes a multiplicative gate on the SSM output; the Mamba-2 review
+# (section 3-2, item 5) adds a NormFormer-style extra normalization there.  The
+# pages name neither the activation, the convolution width nor the norm; the
+# readings used here (SiLU, a depthwise causal convolution whose last tap
+# multiplies the current token, RMSNorm with a per-channel weight over groups of
+# channels) are listed with the other readings of the pages in the design notes.
+
+def silu(v):
+    """v * logistic(v) in fp64, with logistic(v) = (1 + tanh(v / 2)) / 2 (no overflow)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v * 0.5 * (1.0 + np.tanh(0.5 * v))
+
+
+def causal_conv1d(xbc, weight, bias=None, activation: bool = False, conv_state=None, cu_seqlens=None):
+    """Depthwise causal convolution over the token axis, per sequence, in fp64.
+
+    xbc [batch, seqlen, channels]; weight [channels, width]; bias [channels] or
+    None.  For a token t of a sequence starting at token a,
+        out[t, c] = bias[c] + sum_k weight[c, k] * u[t - (width - 1) + k, c],
+    where u is the sequence's input, preceded by the width-1 rows of
+    conv_state[s] (the previous segment's last inputs), or by zeros without a
+    state.  SiLU is applied after the bias when `activation`.  With cu_seqlens
+    (int [nseq + 1]) the batch must be 1 and each [cu[s], cu[s+1]) is one
+    sequence; otherwise each batch row is one.  Returns (out, final_state) with
+    final_state [nseq, width - 1, channels]: each sequence's last width-1 rows
+    of u (taken from its initial state where the sequence is shorter).
+    """
+    x = np.asarray(xbc, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    b_, L, Cc = x.shape
+    W = w.shape[1]
+    assert w.shape[0] == Cc and W >= 1
+    if cu_seqlens is not None:
+        assert b_ == 1
+        cu = [int(v) for v in np.asarray(cu_seqlens)]
+        spans = [(0, cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+    else:
+        spans = [(bi, 0, L) for bi in range(b_)]
+    nseq = len(spans)
+    out = np.zeros_like(x)
+    final = np.zeros((nseq, W - 1, Cc))
+    for s, (bi, a, e) in enumerate(spans):
+        head = (np.zeros((W - 1, Cc)) if conv_state is None
+                else np.asarray(conv_state, dtype=np.float64)[s])
+        u = np.concatenate([head, x[bi, a:e]], axis=0)      # u[W-1 + i] is token a + i
+        for i in range(e - a):
+            acc = np.zeros(Cc) if bias is None else np.asarray(bias, dtype=np.float64).copy()
+            for k in range(W):
+                acc = acc + w[:, k] * u[i + k]
+            out[bi, a + i] = silu(acc) if activation else acc
+        if W > 1:
+            final[s] = u[len(u) - (W - 1):]
+    return out, final
+
+
+def gated_rmsnorm(y, z, weight, eps: float, group_size=None, norm_before_gate: bool = False):
+    """Gated RMSNorm over the last axis, in fp64, per group of `group_size`
+    consecutive channels (the whole axis when None):
+        rms(v) = sqrt(mean over the group of v^2 + eps),
+        norm_before_gate:  out = y / rms(y) * weight * silu(z)
+        otherwise:         out = v / rms(v) * weight,  v = y * silu(z).
+    z may be None (no gate).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    D = y.shape[-1]
+    gs = D if group_size is None else int(group_size)
+    assert D % gs == 0
+    g = np.ones_like(y) if z is None else silu(z)
+    v = y if norm_before_gate else y * g
+    vg = v.reshape(y.shape[:-1] + (D // gs, gs))
+    rms = np.sqrt(np.mean(vg * vg, axis=-1, keepdims=True) + eps)
+    out = (vg / rms).reshape(y.shape) * np.asarray(weight, dtype=np.float64)
+    return out * g if norm_before_gate else out

@@ -347,3 +347,107 @@ def test_dt_preprocess_bias_per_head_and_clamp():
     assert cl.min() >= 0.2 and cl.max() <= 0.9
     inside = (cl > 0.2) & (cl < 0.9)
     np.testing.assert_array_equal(cl[inside], oracle.dt_preprocess(raw, bias, softplus=True)[inside])
+
+
+# ---------------------------------------------------------------- block prologue / epilogue
+def test_silu_pins():
+    """SiLU v*logistic(v): closed values, the exact identity silu(v) - silu(-v) = v,
+    its tails and its slope 1/2 at 0."""
+    v = np.linspace(-30.0, 30.0, 121)
+    assert oracle.silu(np.zeros(1))[0] == 0.0
+    np.testing.assert_allclose(oracle.silu(v) - oracle.silu(-v), v, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.silu(np.array([1.0])), [1.0 / (1.0 + math.exp(-1.0))], rtol=1e-15)
+    assert abs(oracle.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(oracle.silu(np.array([-40.0]))[0]) < 1e-15
+    h = 1e-6
+    assert abs((oracle.silu(np.array([h]))[0] - oracle.silu(np.array([-h]))[0]) / (2 * h) - 0.5) < 1e-9
+
+
+def test_causal_conv1d_closed_forms():
+    rng = np.random.default_rng(21)
+    x = rng.normal(size=(2, 9, 5))
+    # one tap: a per-channel affine map
+    w1 = rng.normal(size=(5, 1))
+    b = rng.normal(size=5)
+    out, fin = oracle.causal_conv1d(x, w1, b)
+    np.testing.assert_allclose(out, x * w1[:, 0] + b, rtol=0, atol=1e-15)
+    assert fin.shape == (2, 0, 5)
+    # impulse response: the taps come out reversed, starting at the impulse
+    w = np.array([[0.5, -0.25, 2.0, 1.5]])
+    imp = np.zeros((1, 12, 1))
+    imp[0, 4, 0] = 1.0
+    out, _ = oracle.causal_conv1d(imp, w)
+    want = np.zeros(12)
+    want[4:8] = w[0, ::-1]
+    np.testing.assert_array_equal(out[0, :, 0], want)
+    # and the activation is SiLU of the biased sum
+    w3 = rng.normal(size=(5, 3))
+    out_n, _ = oracle.causal_conv1d(x, w3, b)
+    out_a, _ = oracle.causal_conv1d(x, w3, b, activation=True)
+    np.testing.assert_allclose(out_a, oracle.silu(out_n), rtol=0, atol=1e-15)
+
+
+def test_causal_conv1d_matches_numpy_convolve():
+    """Without bias and activation each channel is a truncated full convolution
+    with the reversed taps (numpy.convolve)."""
+    rng = np.random.default_rng(22)
+    x = rng.normal(size=(1, 40, 3))
+    w = rng.normal(size=(3, 4))
+    out, _ = oracle.causal_conv1d(x, w)
+    for c in range(3):
+        np.testing.assert_allclose(out[0, :, c], np.convolve(x[0, :, c], w[c, ::-1])[:40], rtol=0, atol=1e-13)
+
+
+def test_causal_conv1d_varlen_split_and_state():
+    rng = np.random.default_rng(23)
+    W, Cc = 4, 6
+    w = rng.normal(size=(Cc, W))
+    b = rng.normal(size=Cc)
+    lens = [5, 1, 0, 9, 2]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = rng.normal(size=(1, int(cu[-1]), Cc))
+    st0 = rng.normal(size=(len(lens), W - 1, Cc))
+    out, fin = oracle.causal_conv1d(x, w, b, True, st0, cu)
+    # packed varlen equals one call per sequence
+    for s in range(len(lens)):
+        a, e = cu[s], cu[s + 1]
+        o_s, f_s = oracle.causal_conv1d(x[:, a:e], w, b, True, st0[s:s + 1])
+        np.testing.assert_array_equal(out[:, a:e], o_s)
+        np.testing.assert_array_equal(fin[s], f_s[0])
+    # a sequence shorter than the window keeps the tail of its initial state
+    np.testing.assert_array_equal(fin[1], np.concatenate([st0[1, 1:], x[0, 5:6]]))
+    np.testing.assert_array_equal(fin[2], st0[2])   # empty sequence: state passes through
+    # splitting a sequence and carrying the state equals the whole
+    xs = rng.normal(size=(2, 17, Cc))
+    whole, fw = oracle.causal_conv1d(xs, w, b, True)
+    p1, f1 = oracle.causal_conv1d(xs[:, :7], w, b, True)
+    p2, f2 = oracle.causal_conv1d(xs[:, 7:], w, b, True, f1)
+    np.testing.assert_allclose(np.concatenate([p1, p2], axis=1), whole, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(f2, fw)
+
+
+def test_gated_rmsnorm_pins():
+    n34 = np.array([0.6, 0.8]) * math.sqrt(2.0)        # [3, 4] / rms([3, 4]), rms = 5 / sqrt(2)
+    one = np.ones(2)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(np.array([3.0, 4.0]), None, one, 0.0), n34, rtol=1e-15)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(np.array([3.0, 4.0]), None, one, 1.0),
+                               np.array([3.0, 4.0]) / math.sqrt(13.5), rtol=1e-15)
+    # gate applied after the norm: a factor silu(z)
+    z = np.array([0.7, -1.3])
+    np.testing.assert_allclose(oracle.gated_rmsnorm(np.array([3.0, 4.0]), z, one, 0.0, norm_before_gate=True),
+                               n34 * oracle.silu(z), rtol=1e-15)
+    # gate applied before the norm: a constant gate cancels up to its sign (eps = 0)
+    zc = np.full(2, 0.9)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(np.array([3.0, 4.0]), zc, one, 0.0), n34, rtol=1e-14)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(np.array([3.0, 4.0]), -zc, one, 0.0), -n34, rtol=1e-14)
+    # groups are normalized independently; the weight scales per channel
+    y = np.array([[3.0, 4.0, 6.0, 8.0, -3.0, -4.0]])
+    wt = np.array([1.0, 2.0, 3.0, 4.0, 5.0, 6.0])
+    out = oracle.gated_rmsnorm(y, None, wt, 0.0, group_size=2)
+    np.testing.assert_allclose(out, np.concatenate([n34, n34, -n34])[None] * wt, rtol=1e-14)
+    # scale invariance with eps = 0
+    rng = np.random.default_rng(24)
+    yy, zz = rng.normal(size=(3, 16)), rng.normal(size=(3, 16))
+    a = oracle.gated_rmsnorm(yy, zz, one.repeat(8), 0.0, group_size=8)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * yy, zz, one.repeat(8), 0.0, group_size=8), a,
+                               rtol=1e-13)
