@@ -12,7 +12,9 @@ The roofline object reports the fused forward kernel against HBM bandwidth
 per-token figures) and, in "mfma", its algorithmic bf16 MFMA rate.  The
 "cpu_baseline" is the fp64 oracle timed on this host's cores over the whole
 workload.  A decode line for the b256 H80 P64 N128 single-token step is
-included under "decode".
+included under "decode", and the block prologue (causal convolution of the
+fused x|B|C projection) and epilogue (gated RMSNorm) at the same 2.7B layer
+shape under "block" (skip with --no-block).
 """
 from __future__ import annotations
 
@@ -56,6 +58,54 @@ def dec_algorithmic(w):
     return float(8 * b * H * P * N + b * H * P * 2 * 2 + b * H * 4 + 2 * b * G * N * 2)
 
 
+def time_calls(fn, stream, nrep=30):
+    """Average µs of fn() over nrep calls, HIP events on `stream`."""
+    import torch
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(nrep):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / nrep * 1e3
+
+
+def bench_block(w, stream, to_dev):
+    """Prologue and epilogue at the forward workload's shape (bf16 io).
+
+    Algorithmic bytes: the convolution reads the fused projection and writes
+    x, B and C once (2 * tokens * channels * 2 bytes; weights negligible); the
+    gated RMSNorm reads y and z and writes its output (3 * tokens * H*P * 2)."""
+    import torch
+    from selective_state_space_71_amd import ssd, workloads as wl
+    b, L, H, P, N, G = w["batch"], w["seqlen"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"]
+    d = wl.make_block_inputs(b, L, H, P, N, G, 4, "bf16", seed=7100, with_state=False)
+    tok = b * L
+    res = {"workload": f"batch {b}, L {L}, {H * P} + 2*{G * N} channels, conv width 4, SiLU; "
+                       f"gated RMSNorm over {H * P} channels, one group, bf16"}
+    xbc = to_dev(d["xbc"], True)
+    cw, cb = to_dev(d["conv_w"], False), to_dev(d["conv_b"], False)
+    x = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    Bo = torch.empty((b, L, G, N), dtype=torch.bfloat16, device="cuda")
+    Co = torch.empty_like(Bo)
+    us = time_calls(lambda: ssd.causal_conv1d_fwd(xbc, cw, H, P, G, N, bias=cb, x=x, B=Bo, C=Co), stream)
+    byts = 2.0 * tok * (H * P + 2 * G * N) * 2
+    res["conv"] = {"us": us, "alg_bytes": byts, "achieved_gbs": byts / (us * 1e-6) / 1e9,
+                   "peak_gbs": HBM_PEAK_GBS, "frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    del xbc, x, Bo, Co
+    y, z = to_dev(d["y"], True), to_dev(d["z"], True)
+    nw = to_dev(d["norm_w"], False)
+    o = torch.empty_like(y)
+    us = time_calls(lambda: ssd.gated_rmsnorm_fwd(y, z, nw, eps=1e-5, out=o), stream)
+    byts = 3.0 * tok * H * P * 2
+    res["gated_rmsnorm"] = {"us": us, "alg_bytes": byts, "achieved_gbs": byts / (us * 1e-6) / 1e9,
+                            "peak_gbs": HBM_PEAK_GBS, "frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     for f in ("ssd_fwd_kernel.h", "ssd_device.h", "ssd_fwd_launch.h"):
@@ -85,6 +135,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
@@ -202,6 +253,9 @@ def main():
                          "achieved_gbs": db / (us * 1e-6) / 1e9, "peak_gbs": HBM_PEAK_GBS,
                          "frac": db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
         del st, dx, dB, dC, ddt, dA, dD, dy
+
+    if not args.no_block:
+        out["block"] = bench_block(w, stream, to_dev)
 
     if not args.no_cpu_baseline:
         from oracle import oracle

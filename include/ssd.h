@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
     SSD_OK = 0,
@@ -209,6 +209,77 @@ ssd_status_t ssd_decode_step_ex(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
                                 const void *x, const float *dt, const float *A,
                                 const void *B, const void *C, const float *D,
                                 void *y, void *stream);
+
+/*
+ * Block prologue: the short causal convolution and activation that the Mamba
+ * block applies to one projected branch before the selective SSM
+ * ("Mamba - Linear-Time Sequence Modeling with Selective State Spaces" review,
+ * feghi.github.io, section 5, the block figure read bottom to top), here over
+ * the fused x | B | C projection of the Mamba-2 block ("Transformers are SSMs
+ * Review", section 3-2, item 5: the data-dependent projections are made in
+ * parallel at the start of the block).  Depthwise, per sequence:
+ *
+ *     u[t, c]   = the channel-c input of token t of the sequence, preceded by
+ *                 the width-1 rows of conv_state (zeros when conv_state is NULL)
+ *     out[t, c] = act(bias[c] + sum_{k<width} weight[c, k] * u[t - (width-1) + k, c])
+ *
+ * (the last tap multiplies the current token), act = SiLU (v / (1 + e^-v))
+ * when `silu` is nonzero, else the identity.  fp32 arithmetic, io output
+ * rounded to nearest even.
+ *
+ *   dims        host pointer; batch, seqlen, nheads, headdim, dstate, ngroups,
+ *               nseq as for ssd_chunk_scan_fwd (nseq == batch for a dense
+ *               batch; batch == 1 with cu_seqlens).
+ *   width       number of taps, 1..4.
+ *   xbc         [batch, seqlen, channels] io, channels = nheads*headdim +
+ *               2*ngroups*dstate in the order x | B | C.
+ *   weight      [channels, width] fp32;  bias [channels] fp32 or NULL.
+ *   conv_state  [nseq, width-1, channels] io or NULL: the width-1 inputs that
+ *               precede each sequence (a previous segment's conv_state_out).
+ *   cu_seqlens  as for ssd_chunk_scan_fwd (device int32, or NULL).
+ *   x           [batch, seqlen, nheads, headdim] io output (channels x);
+ *   B, C        [batch, seqlen, ngroups, dstate] io outputs (channels B, C):
+ *               the layouts ssd_chunk_scan_fwd reads.
+ *   conv_state_out  [nseq, width-1, channels] io or NULL: each sequence's last
+ *               width-1 rows of u (its initial state rows where it is shorter,
+ *               the initial state itself for an empty packed sequence).
+ *
+ * Supported: headdim and dstate multiples of 8.  Pointers 16-byte aligned
+ * (cu_seqlens 4).  The outputs must not overlap each other or any input
+ * (conv_state_out must not be conv_state: SSD_ERR_ALIAS).
+ */
+ssd_status_t ssd_causal_conv1d_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype, int32_t width,
+                                   const void *xbc, const float *weight, const float *bias,
+                                   int32_t silu, const void *conv_state, const int32_t *cu_seqlens,
+                                   void *x, void *B, void *C, void *conv_state_out, void *stream);
+
+/*
+ * Block epilogue: the multiplicative gate of the Mamba block's second branch
+ * (feghi.github.io review, section 5) with the NormFormer-style extra
+ * normalization of Mamba-2 ("Transformers are SSMs Review", section 3-2,
+ * item 5), as RMSNorm over groups of `group_size` consecutive channels:
+ *
+ *     rms(v) = sqrt(mean over the group of v^2 + eps)
+ *     norm_before_gate == 0:  out = v / rms(v) * weight,  v = y * silu(z)
+ *     norm_before_gate != 0:  out = y / rms(y) * weight * silu(z)
+ *
+ * fp32 arithmetic, io output rounded to nearest even.
+ *
+ *   rows        number of token rows (batch * seqlen).
+ *   dim         channels per row (nheads * headdim);  group_size divides dim.
+ *   y           [rows, dim] io (the SSD output);  z [rows, dim] io gate input,
+ *               or NULL for a plain RMSNorm.
+ *   weight      [dim] fp32.   eps >= 0 and finite (eps = 0 with an all-zero
+ *               group gives NaN, as the formula does).
+ *   out         [rows, dim] io output; may be y or z itself (in place), must
+ *               not overlap them otherwise, nor weight.
+ *
+ * Supported: group_size a multiple of 8, at most 8192 channels (bf16) or
+ * 4096 (fp32).  Pointers 16-byte aligned.
+ */
+ssd_status_t ssd_gated_rmsnorm_fwd(int64_t rows, int32_t dim, int32_t group_size, ssd_dtype_t io_dtype,
+                                   const void *y, const void *z, const float *weight, float eps,
+                                   int32_t norm_before_gate, void *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,10 +6,12 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <utility>
 
 #include "ssd.h"
 #include "ssd_device.h"
 #include "ssd_fwd_kernel.h"
+#include "ssd_block_kernels.h"
 
 namespace ssd {
 bool fwd_dispatch_bf16(int p, int n, int q, const FwdParams &prm, long long max_entries, hipStream_t st,
@@ -267,6 +269,41 @@ static bool decode_launch(int N, const DecodeParams &prm, unsigned grid, hipStre
     case 256: hipLaunchKernelGGL((ssd_decode_kernel<IO, 256>), dim3(grid), dim3(256), 0, st, prm); return true;
     default: return false;
     }
+}
+
+template <typename IO>
+static bool conv_launch(int width, const ConvParams &p, dim3 grid, hipStream_t st) {
+    switch (width) {
+    case 1: hipLaunchKernelGGL((ssd_conv1d_kernel<IO, 1>), grid, dim3(256), 0, st, p); return true;
+    case 2: hipLaunchKernelGGL((ssd_conv1d_kernel<IO, 2>), grid, dim3(256), 0, st, p); return true;
+    case 3: hipLaunchKernelGGL((ssd_conv1d_kernel<IO, 3>), grid, dim3(256), 0, st, p); return true;
+    case 4: hipLaunchKernelGGL((ssd_conv1d_kernel<IO, 4>), grid, dim3(256), 0, st, p); return true;
+    default: return false;
+    }
+}
+
+template <typename IO, int NCH>
+static bool norm_try(int nch, int mode, const NormParams &p, unsigned blocks, hipStream_t st) {
+    if (nch != NCH) return false;
+    switch (mode) {
+    case 0: hipLaunchKernelGGL((ssd_gated_norm_kernel<IO, NCH, 0>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((ssd_gated_norm_kernel<IO, NCH, 1>), dim3(blocks), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((ssd_gated_norm_kernel<IO, NCH, 2>), dim3(blocks), dim3(256), 0, st, p); break;
+    }
+    return true;
+}
+
+template <typename IO, int... NCH>
+static bool norm_dispatch(int nch, int mode, const NormParams &p, unsigned blocks, hipStream_t st,
+                          std::integer_sequence<int, NCH...>) {
+    return (norm_try<IO, NCH + 1>(nch, mode, p, blocks, st) || ...);
+}
+
+// one wave per (row, group), 512 channels per register chunk: 1..16 chunks
+// for bf16 io, 1..8 for fp32; mode 0 no gate, 1 gate before the norm, 2 after
+template <typename IO>
+static bool norm_launch(int nch, int mode, const NormParams &p, unsigned blocks, hipStream_t st) {
+    return norm_dispatch<IO>(nch, mode, p, blocks, st, std::make_integer_sequence<int, sizeof(IO) == 2 ? 16 : 8>{});
 }
 
 }  // namespace ssd
@@ -608,6 +645,112 @@ ssd_status_t ssd_decode_step_ex(const ssd_dims_t *dims, ssd_dtype_t io, const ss
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool ok = (io == SSD_BF16) ? ssd::decode_launch<ssd::bf16>(N, p, (unsigned)units, s)
                                      : ssd::decode_launch<float>(N, p, (unsigned)units, s);
+    if (!ok) return SSD_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+
+ssd_status_t ssd_causal_conv1d_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t width, const void *xbc,
+                                   const float *weight, const float *bias, int32_t silu, const void *conv_state,
+                                   const int32_t *cu_seqlens, void *x, void *B, void *C, void *conv_state_out,
+                                   void *stream) {
+    if (!dims) return SSD_ERR_NULL_PTR;
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
+    const ssd_dims_t &d = *dims;
+    if (!dims_ok(d)) return SSD_ERR_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? d.batch != 1 : d.nseq != d.batch) return SSD_ERR_SHAPE;
+    if (width < 1 || width > 4 || d.headdim % 8 != 0 || d.dstate % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (!xbc || !weight || !x || !B || !C) return SSD_ERR_NULL_PTR;
+    const void *al16[] = {xbc, weight, bias, conv_state, x, B, C, conv_state_out};
+    for (const void *p : al16)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
+    const long long tokens = (long long)d.batch * d.seqlen;
+    const long long HP = (long long)d.nheads * d.headdim, GN = (long long)d.ngroups * d.dstate;
+    const long long Cc = HP + 2 * GN;
+    if (Cc > INT_MAX / 8 || tokens > (long long)INT_MAX) return SSD_ERR_SHAPE;
+    const size_t E = (io == SSD_BF16) ? 2 : 4;
+    const size_t nst = (size_t)d.nseq * (width - 1) * Cc * E;
+    const Range rin = rng(xbc, tokens * Cc * E), rw = rng(weight, Cc * width * 4),
+                rb = rng(bias, bias ? Cc * 4 : 0), rs = rng(conv_state, conv_state ? nst : 0),
+                rcu = rng(cu_seqlens, varlen ? (size_t)(d.nseq + 1) * 4 : 0);
+    const Range rx = rng(x, tokens * HP * E), rB = rng(B, tokens * GN * E), rC = rng(C, tokens * GN * E),
+                rso = rng(conv_state_out, conv_state_out ? nst : 0);
+    for (Range o : {rx, rB, rC, rso}) {
+        for (Range i : {rin, rw, rb, rs, rcu})
+            if (overlap(o, i)) return SSD_ERR_ALIAS;
+    }
+    if (overlap(rx, rB) || overlap(rx, rC) || overlap(rB, rC) || overlap(rso, rx) || overlap(rso, rB) ||
+        overlap(rso, rC))
+        return SSD_ERR_ALIAS;
+    ssd::ConvParams p{};
+    p.xbc = xbc;
+    p.w = weight;
+    p.bias = bias;
+    p.state_in = conv_state;
+    p.cu_seqlens = cu_seqlens;
+    p.x = x;
+    p.B = B;
+    p.C = C;
+    p.state_out = conv_state_out;
+    p.tokens = tokens;
+    p.seqlen = d.seqlen;
+    p.nseq = d.nseq;
+    p.Cc = (int)Cc;
+    p.HP = (int)HP;
+    p.GN = (int)GN;
+    p.silu = silu != 0;
+    // 64 tokens per thread, more when the grid would exceed its y limit
+    long long run = 64;
+    while ((tokens + run * 4 - 1) / (run * 4) > 65535) run *= 2;
+    p.run = (int)run;
+    const dim3 grid((unsigned)((Cc / 8 + 63) / 64), (unsigned)((tokens + run * 4 - 1) / (run * 4)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool ok = (io == SSD_BF16) ? ssd::conv_launch<ssd::bf16>(width, p, grid, st)
+                                     : ssd::conv_launch<float>(width, p, grid, st);
+    if (!ok) return SSD_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_gated_rmsnorm_fwd(int64_t rows, int32_t dim, int32_t group_size, ssd_dtype_t io, const void *y,
+                                   const void *z, const float *weight, float eps, int32_t norm_before_gate,
+                                   void *out, void *stream) {
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
+    if (rows < 1 || dim < 1 || group_size < 1 || dim % group_size != 0) return SSD_ERR_SHAPE;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return SSD_ERR_SHAPE;
+    if (group_size % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    const int nch = (group_size + 511) / 512;
+    if (nch > ((io == SSD_BF16) ? 16 : 8)) return SSD_ERR_UNSUPPORTED;
+    if (!y || !weight || !out) return SSD_ERR_NULL_PTR;
+    const void *al16[] = {y, z, weight, out};
+    for (const void *p : al16)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
+    const long long groups = dim / group_size;
+    const long long units = rows * groups;
+    if (rows > LLONG_MAX / dim || (units + 3) / 4 > (long long)INT_MAX) return SSD_ERR_SHAPE;
+    const size_t E = (io == SSD_BF16) ? 2 : 4;
+    const size_t bytes = (size_t)rows * dim * E;
+    const Range ry = rng(y, bytes), rz = rng(z, z ? bytes : 0), rw = rng(weight, (size_t)dim * 4), ro = rng(out, bytes);
+    // out may be y or z itself (every group is read whole before it is written)
+    if (overlap(ro, rw) || (overlap(ro, ry) && out != y) || (overlap(ro, rz) && out != z)) return SSD_ERR_ALIAS;
+    ssd::NormParams p{};
+    p.y = y;
+    p.z = z;
+    p.w = weight;
+    p.out = out;
+    p.units = units;
+    p.dim = dim;
+    p.gs = group_size;
+    p.groups = (int)groups;
+    p.eps = eps;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const unsigned blocks = (unsigned)((units + 3) / 4);
+    const int mode = z ? (norm_before_gate ? 2 : 1) : 0;
+    const bool ok = (io == SSD_BF16) ? ssd::norm_launch<ssd::bf16>(nch, mode, p, blocks, st)
+                                     : ssd::norm_launch<float>(nch, mode, p, blocks, st);
     if (!ok) return SSD_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;

@@ -99,6 +99,16 @@ def load_library(path: str = LIB_PATH):
         ctypes.POINTER(SsdDims), ctypes.c_int,
         _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
     ]
+    lib.ssd_causal_conv1d_fwd.restype = ctypes.c_int
+    lib.ssd_causal_conv1d_fwd.argtypes = [
+        ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP,
+        _VP, _VP, _VP, _VP, _VP,
+    ]
+    lib.ssd_gated_rmsnorm_fwd.restype = ctypes.c_int
+    lib.ssd_gated_rmsnorm_fwd.argtypes = [
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _VP, _VP, _VP, ctypes.c_float,
+        ctypes.c_int32, _VP, _VP,
+    ]
     _lib = lib
     return lib
 
@@ -248,3 +258,78 @@ def decode_step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus
     if code != 0:
         raise SsdError(code, "ssd_decode_step_ex")
     return y
+
+
+def causal_conv1d_fwd(xbc, weight, nheads: int, headdim: int, ngroups: int, dstate: int, bias=None,
+                      silu: bool = True, conv_state=None, cu_seqlens=None, return_final_state: bool = False,
+                      x=None, B=None, C=None, conv_state_out=None):
+    """Block prologue through ``ssd_causal_conv1d_fwd``: depthwise causal
+    convolution of the fused x | B | C projection ``xbc`` [batch, seqlen,
+    channels] with ``weight`` [channels, width] (fp32), split into x [batch,
+    seqlen, nheads, headdim] and B, C [batch, seqlen, ngroups, dstate].
+    Returns (x, B, C) or (x, B, C, conv_state_out)."""
+    lib = load_library()
+    dev = xbc.device
+    _need(xbc, "xbc", device=dev)
+    io = _io_code(xbc)
+    if xbc.dim() != 3:
+        raise ValueError("xbc must be [batch, seqlen, channels]")
+    b, L, Cc = xbc.shape
+    HP, GN = nheads * headdim, ngroups * dstate
+    if Cc != HP + 2 * GN:
+        raise ValueError(f"xbc has {Cc} channels, expected {HP + 2 * GN}")
+    if weight.dim() != 2:
+        raise ValueError("weight must be [channels, width]")
+    W = weight.shape[1]
+    _need(weight, "weight", torch.float32, (Cc, W), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (Cc,), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    nseq = b if cu_seqlens is None else cu_seqlens.numel() - 1
+    if conv_state is not None:
+        _need(conv_state, "conv_state", xbc.dtype, (nseq, W - 1, Cc), dev)
+    x = torch.empty((b, L, nheads, headdim), dtype=xbc.dtype, device=dev) if x is None else x
+    B = torch.empty((b, L, ngroups, dstate), dtype=xbc.dtype, device=dev) if B is None else B
+    C = torch.empty((b, L, ngroups, dstate), dtype=xbc.dtype, device=dev) if C is None else C
+    _need(x, "x", xbc.dtype, (b, L, nheads, headdim), dev)
+    _need(B, "B", xbc.dtype, (b, L, ngroups, dstate), dev)
+    _need(C, "C", xbc.dtype, (b, L, ngroups, dstate), dev)
+    if conv_state_out is None and return_final_state:
+        conv_state_out = torch.empty((nseq, W - 1, Cc), dtype=xbc.dtype, device=dev)
+    elif conv_state_out is not None:
+        _need(conv_state_out, "conv_state_out", xbc.dtype, (nseq, W - 1, Cc), dev)
+    dims = SsdDims(b, L, nheads, headdim, dstate, ngroups, nseq)
+    code = lib.ssd_causal_conv1d_fwd(ctypes.byref(dims), io, W, _ptr(xbc), _ptr(weight), _ptr(bias),
+                                     1 if silu else 0, _ptr(conv_state), _ptr(cu_seqlens), _ptr(x), _ptr(B),
+                                     _ptr(C), _ptr(conv_state_out), _stream(dev))
+    if code != 0:
+        raise SsdError(code, "ssd_causal_conv1d_fwd")
+    return (x, B, C, conv_state_out) if return_final_state else (x, B, C)
+
+
+def gated_rmsnorm_fwd(y, z, weight, eps: float = 1e-5, group_size=None, norm_before_gate: bool = False,
+                      out=None):
+    """Block epilogue through ``ssd_gated_rmsnorm_fwd``: RMSNorm over groups of
+    ``group_size`` channels of the last axis of y * silu(z) (or of y, gated
+    after the norm), times ``weight``.  ``y`` may be [..., nheads, headdim]:
+    the channels are its last two axes.  ``out`` may be ``y`` (in place)."""
+    lib = load_library()
+    dev = y.device
+    _need(y, "y", device=dev)
+    io = _io_code(y)
+    dim = weight.numel()
+    if y.numel() % dim != 0 or y.shape[-1] > dim or dim % y.shape[-1] != 0:
+        raise ValueError("the trailing axes of y must hold the weight's channels")
+    rows = y.numel() // dim
+    _need(weight, "weight", torch.float32, None, dev)
+    if z is not None:
+        _need(z, "z", y.dtype, tuple(y.shape), dev)
+    out = torch.empty_like(y) if out is None else out
+    _need(out, "out", y.dtype, tuple(y.shape), dev)
+    gs = dim if group_size is None else int(group_size)
+    code = lib.ssd_gated_rmsnorm_fwd(rows, dim, gs, io, _ptr(y), _ptr(z), _ptr(weight), float(eps),
+                                     1 if norm_before_gate else 0, _ptr(out), _stream(dev))
+    if code != 0:
+        raise SsdError(code, "ssd_gated_rmsnorm_fwd")
+    return out

@@ -194,3 +194,40 @@ def workload_inputs(index: int):
                            w["ngroups"], w["io"], seed, w["init_std"], lengths=lens)
     return make_inputs(w["batch"], w["seqlen"], w["nheads"], w["headdim"], w["dstate"],
                        w["ngroups"], w["io"], seed, w["init_std"])
+
+
+def make_block_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                      ngroups: int = 1, width: int = 4, io: str = "bf16", seed: int = 0,
+                      lengths=None, with_state: bool = True):
+    """Draw inputs for the block prologue and epilogue.
+
+    Prologue: xbc [b, L, H*P + 2*G*N] in the io dtype (the fused projection
+    output, N(0, 1)), conv weight [channels, width] and bias [channels] in
+    float32 drawn U(-1/sqrt(width), 1/sqrt(width)) (the default initialisation
+    of a depthwise convolution with `width` inputs per output), conv_state
+    [nseq, width-1, channels] in the io dtype (N(0, 1)) or None.
+    Epilogue: y and z [b, L, H*P] in the io dtype (N(0, 1)) and the norm weight
+    [H*P] float32 ~ 1 + N(0, 0.1^2).  With ``lengths`` the batch is 1 and the
+    sequences are packed (cu_seqlens)."""
+    rng = np.random.default_rng(seed)
+    b, L = batch, seqlen
+    HP, GN = nheads * headdim, ngroups * dstate
+    Cc = HP + 2 * GN
+    bound = np.float32(1.0 / math.sqrt(width))
+    cu = None
+    nseq = b
+    if lengths is not None:
+        assert b == 1 and int(np.sum(lengths)) == L
+        cu = np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+        nseq = len(lengths)
+    return dict(
+        xbc=_round_io(rng.standard_normal((b, L, Cc), dtype=np.float32), io),
+        conv_w=rng.uniform(-bound, bound, size=(Cc, width)).astype(np.float32),
+        conv_b=rng.uniform(-bound, bound, size=Cc).astype(np.float32),
+        conv_state=(_round_io(rng.standard_normal((nseq, width - 1, Cc), dtype=np.float32), io)
+                    if with_state else None),
+        y=_round_io(rng.standard_normal((b, L, HP), dtype=np.float32), io),
+        z=_round_io(rng.standard_normal((b, L, HP), dtype=np.float32), io),
+        norm_w=(1.0 + 0.1 * rng.standard_normal(HP)).astype(np.float32),
+        cu_seqlens=cu, io=io, batch=b, seqlen=L, nheads=nheads, headdim=headdim, dstate=dstate,
+        ngroups=ngroups, width=width, nseq=nseq)

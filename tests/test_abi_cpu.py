@@ -24,7 +24,8 @@ def test_header_symbols_are_exported(lib):
     names = ssd.header_functions()
     assert {"ssd_chunk_scan_fwd", "ssd_decode_step", "ssd_chunk_scan_fwd_workspace_size",
             "ssd_status_string", "ssd_abi_version", "ssd_chunk_scan_fwd_check",
-            "ssd_chunk_scan_fwd_ex", "ssd_decode_step_ex"} <= set(names)
+            "ssd_chunk_scan_fwd_ex", "ssd_decode_step_ex", "ssd_causal_conv1d_fwd",
+            "ssd_gated_rmsnorm_fwd"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -34,7 +35,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 2
+    assert lib.ssd_abi_version() == 3
     for code, name in ssd._STATUS.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(77)
@@ -164,6 +165,63 @@ def test_dt_options_validation(lib, opts, expect):
     assert rc == expect
 
 
+def _conv(lib, dims, io=ssd.SSD_BF16, width=4, **ptrs):
+    dp = dict(xbc=FAKE, w=FAKE + (1 << 34), b=None, st=None, cu=None, x=FAKE + (2 << 34), B=FAKE + (3 << 34),
+              C=FAKE + (4 << 34), so=None)
+    dp.update(ptrs)
+    return lib.ssd_causal_conv1d_fwd(ctypes.byref(dims) if dims is not None else None, io, width, dp["xbc"],
+                                     dp["w"], dp["b"], 1, dp["st"], dp["cu"], dp["x"], dp["B"], dp["C"],
+                                     dp["so"], None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), 1),
+    (dict(io=4), 3),
+    (dict(width=0), 4),
+    (dict(width=5), 4),
+    (dict(dims=_dims(headdim=12)), 4),
+    (dict(dims=_dims(dstate=20)), 4),
+    (dict(dims=_dims(nseq=3)), 2),                               # dense needs nseq == batch
+    (dict(cu=FAKE + (5 << 34)), 2),                              # varlen needs batch == 1
+    (dict(x=None), 1),
+    (dict(w=None), 1),
+    (dict(B=FAKE + (3 << 34) + 8), 5),
+    (dict(x=FAKE + 64), 6),                                      # x overlaps xbc
+    (dict(C=FAKE + (3 << 34) + 64), 6),                          # C overlaps B
+    (dict(st=FAKE + (6 << 34), so=FAKE + (6 << 34)), 6),         # state out over state in
+])
+def test_conv_validation_rejects(lib, case, expect):
+    dims = case.pop("dims", _dims())
+    assert _conv(lib, dims, **case) == expect
+
+
+def _norm(lib, rows=16, dim=5120, gs=5120, io=ssd.SSD_BF16, eps=1e-5, **ptrs):
+    dp = dict(y=FAKE, z=FAKE + (1 << 34), w=FAKE + (2 << 34), out=FAKE + (3 << 34))
+    dp.update(ptrs)
+    return lib.ssd_gated_rmsnorm_fwd(rows, dim, gs, io, dp["y"], dp["z"], dp["w"], ctypes.c_float(eps), 0,
+                                     dp["out"], None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(io=2), 3),
+    (dict(rows=0), 2),
+    (dict(gs=1000), 2),                                          # does not divide dim
+    (dict(dim=60, gs=12), 4),                                    # not a multiple of 8
+    (dict(dim=16384, gs=16384), 4),                              # bf16 groups up to 8192
+    (dict(dim=8192, gs=8192, io=ssd.SSD_F32), 4),                # fp32 groups up to 4096
+    (dict(eps=-1.0), 2),
+    (dict(eps=float("nan")), 2),
+    (dict(y=None), 1),
+    (dict(w=None), 1),
+    (dict(out=FAKE + (3 << 34) + 4), 5),
+    (dict(out=FAKE + 64), 6),                                    # partial overlap with y
+    (dict(out=FAKE + (2 << 34)), 6),                             # over the weight
+])
+def test_norm_validation_rejects(lib, case, expect):
+    assert _norm(lib, **case) == expect
+
+
+# (last: it reloads the binding module, which redefines its ctypes structures)
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.reload(ssd)
