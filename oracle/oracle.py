@@ -228,3 +228,75 @@ def gated_rmsnorm(y, z, weight, eps: float, group_size=None, norm_before_gate: b
     rms = np.sqrt(np.mean(vg * vg, axis=-1, keepdims=True) + eps)
     out = (vg / rms).reshape(y.shape) * np.asarray(weight, dtype=np.float64)
     return out * g if norm_before_gate else out
+
+
+# --------------------------------------------------------------------------
+# Backward pass.
+#
+# The gradient of a scalar loss through the recurrence of ssd_fwd (bdev.io,
+# problem section: h_t = Abar_t h_{t-1} + Bbar_t x_t, y_t = C_t^T h_t; the
+# textbook chapter's section 1 and 3 discretisation with a scalar decay per
+# head), written out as the adjoint recurrence that runs backwards over the
+# tokens: with g_t = dL/dh_t,
+#     g_t      = dy_t C_t^T + Abar_{t+1} g_{t+1}      (g_last = dy_last C^T + dfinal)
+#     dx_t     = D dy_t + dt_t g_t B_t
+#     dB_t    += dt_t g_t^T x_t            (summed over the heads of B's group)
+#     dC_t    += h_t^T dy_t                (likewise)
+#     q_t      = <g_t, Abar_t h_{t-1}>     (Frobenius product)
+#     ddt_t    = x_t^T g_t B_t + A q_t
+#     dA      += dt_t q_t
+#     dD      += dy_t . x_t
+#     dinit    = Abar_first g_first
+# The pages do not print a backward pass; this is reverse-mode
+# differentiation of the forward above, pinned against finite differences of
+# the C oracle in the tests.
+
+def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal=None):
+    """fp64 gradients of L = <dy, y> + <dfinal, final_state> for y, final_state
+    = ssd_fwd(x, dt, A, B, C, D, init_state, cu_seqlens).
+
+    Shapes as for ssd_fwd; dy like y, dfinal like final_state (or None).
+    Returns a dict with dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC
+    [b, L, G, N], dD [H] and dinit [nseq, H, P, N]."""
+    x = _f64(x); dt = _f64(dt); A = _f64(A); B = _f64(B); C = _f64(C); dy = _f64(dy)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    hpg = H // G
+    Dv = np.zeros(H) if D is None else _f64(D)
+    if cu_seqlens is None:
+        spans = [(bi, 0, L) for bi in range(b)]
+    else:
+        assert b == 1
+        cu = [int(v) for v in np.asarray(cu_seqlens)]
+        spans = [(0, cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+    nseq = len(spans)
+    init = np.zeros((nseq, H, P, N)) if init_state is None else _f64(init_state)
+    dfin = np.zeros((nseq, H, P, N)) if dfinal is None else _f64(dfinal)
+    out = dict(dx=np.zeros_like(x), ddt=np.zeros_like(dt), dA=np.zeros(H), dB=np.zeros_like(B),
+               dC=np.zeros_like(C), dD=np.zeros(H), dinit=np.zeros((nseq, H, P, N)))
+    for s, (bi, a, e) in enumerate(spans):
+        for h in range(H):
+            g_ = h // hpg
+            # forward, keeping every state
+            hs = np.zeros((e - a + 1, P, N))
+            hs[0] = init[s, h]
+            for i, t in enumerate(range(a, e)):
+                abar = np.exp(dt[bi, t, h] * A[h])
+                hs[i + 1] = abar * hs[i] + dt[bi, t, h] * np.outer(x[bi, t, h], B[bi, t, g_])
+            # backward
+            g = dfin[s, h].copy()
+            for i in range(e - a - 1, -1, -1):
+                t = a + i
+                abar = np.exp(dt[bi, t, h] * A[h])
+                g = g + np.outer(dy[bi, t, h], C[bi, t, g_])          # dL/dh_t
+                out["dC"][bi, t, g_] += hs[i + 1].T @ dy[bi, t, h]
+                gB = g @ B[bi, t, g_]
+                out["dx"][bi, t, h] += Dv[h] * dy[bi, t, h] + dt[bi, t, h] * gB
+                out["dB"][bi, t, g_] += dt[bi, t, h] * (g.T @ x[bi, t, h])
+                q = float(np.sum(g * (abar * hs[i])))
+                out["ddt"][bi, t, h] += float(x[bi, t, h] @ gB) + A[h] * q
+                out["dA"][h] += dt[bi, t, h] * q
+                out["dD"][h] += float(dy[bi, t, h] @ x[bi, t, h])
+                g = abar * g                                            # dL/dh_{t-1}
+            out["dinit"][s, h] = g
+    return out

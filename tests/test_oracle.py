@@ -451,3 +451,64 @@ def test_gated_rmsnorm_pins():
     a = oracle.gated_rmsnorm(yy, zz, one.repeat(8), 0.0, group_size=8)
     np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * yy, zz, one.repeat(8), 0.0, group_size=8), a,
                                rtol=1e-13)
+
+
+# ---------------------------------------------------------------- backward
+def _bwd_problem(seed, b=1, L=7, H=2, P=3, N=4, G=1, lengths=None):
+    rng = np.random.default_rng(seed)
+    nseq = b if lengths is None else len(lengths)
+    p = dict(x=rng.normal(size=(b, L, H, P)), dt=rng.uniform(0.05, 0.6, size=(b, L, H)),
+             A=-rng.uniform(0.3, 2.0, size=H), B=rng.normal(size=(b, L, G, N)) * 0.5,
+             C=rng.normal(size=(b, L, G, N)) * 0.5, D=rng.normal(size=H),
+             init_state=rng.normal(size=(nseq, H, P, N)))
+    cu = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    dy = rng.normal(size=(b, L, H, P))
+    dfin = rng.normal(size=(nseq, H, P, N))
+    return p, cu, dy, dfin
+
+
+def _loss(p, cu, dy, dfin):
+    y, fin = oracle.ssd_fwd(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], init_state=p["init_state"],
+                            cu_seqlens=cu)
+    return float(np.sum(dy * y) + np.sum(dfin * fin))
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(H=2, G=2), dict(L=9, lengths=[4, 0, 5])])
+def test_backward_matches_finite_differences(kw):
+    """Every gradient of the adjoint oracle against central differences of the
+    (independent) C forward oracle."""
+    p, cu, dy, dfin = _bwd_problem(31, **kw)
+    g = oracle.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], dy, D=p["D"], init_state=p["init_state"],
+                       cu_seqlens=cu, dfinal=dfin)
+    names = dict(x="dx", dt="ddt", A="dA", B="dB", C="dC", D="dD", init_state="dinit")
+    eps = 1e-6
+    for k, gk in names.items():
+        fd = np.zeros_like(p[k])
+        for idx in np.ndindex(p[k].shape):
+            keep = p[k][idx]
+            p[k][idx] = keep + eps
+            lp = _loss(p, cu, dy, dfin)
+            p[k][idx] = keep - eps
+            lm = _loss(p, cu, dy, dfin)
+            p[k][idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gk], fd, rtol=1e-6, atol=1e-7, err_msg=k)
+
+
+def test_backward_euler_identities():
+    """y and final_state are jointly linear in (x, init) and linear in B and in
+    C, so the gradient contracted with the input returns the loss exactly."""
+    p, _, dy, dfin = _bwd_problem(32, b=2, L=64, H=4, P=8, N=16, G=2)
+    y, fin = oracle.ssd_fwd(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], init_state=p["init_state"])
+    g = oracle.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], dy, D=p["D"], init_state=p["init_state"],
+                       dfinal=dfin)
+    L_all = np.sum(dy * y) + np.sum(dfin * fin)
+    assert abs(np.sum(g["dx"] * p["x"]) + np.sum(g["dinit"] * p["init_state"]) - L_all) < 1e-9 * abs(L_all) + 1e-9
+    # B and C: without the initial state and D, y and final_state are linear in each
+    y0, fin0 = oracle.ssd_fwd(p["x"], p["dt"], p["A"], p["B"], p["C"])
+    g0 = oracle.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], dy, dfinal=dfin)
+    L0 = np.sum(dy * y0) + np.sum(dfin * fin0)
+    assert abs(np.sum(g0["dB"] * p["B"]) - L0) < 1e-9 * abs(L0) + 1e-9
+    assert abs(np.sum(g0["dC"] * p["C"]) - np.sum(dy * y0)) < 1e-9 * abs(L0) + 1e-9
+    # dD is the plain contraction of dy with x
+    np.testing.assert_allclose(g["dD"], np.einsum("blhp,blhp->h", dy, p["x"]), rtol=1e-12)
