@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
     SSD_OK = 0,
@@ -280,6 +280,47 @@ ssd_status_t ssd_causal_conv1d_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
 ssd_status_t ssd_gated_rmsnorm_fwd(int64_t rows, int32_t dim, int32_t group_size, ssd_dtype_t io_dtype,
                                    const void *y, const void *z, const float *weight, float eps,
                                    int32_t norm_before_gate, void *out, void *stream);
+
+/*
+ * Backward pass of ssd_chunk_scan_fwd: the gradients of
+ *     L = <dy, y> + <dfinal_state, final_state>
+ * with respect to x, dt, A, B, C, D and init_state, through the same chunked
+ * evaluation ("Transformers are SSMs Review", section 3-2(4)); the pages
+ * print no backward pass, so this is reverse-mode differentiation of that
+ * forward (the chunk-boundary states are recomputed, and the state gradients
+ * are chained backwards over the chunks; 64-token chunks internally, which
+ * changes only the rounding).
+ *
+ *   dims, io_dtype, x, dt, A, B, C, D, init_state, cu_seqlens: as for the
+ *               forward call whose gradient is wanted (dt is the final step
+ *               size; chain any preprocessing through the caller).
+ *   dy          [batch, seqlen, nheads, headdim] io
+ *   dfinal_state [nseq, nheads, headdim, dstate] fp32, or NULL (zero)
+ *   dx          [batch, seqlen, nheads, headdim] io output
+ *   ddt         [batch, seqlen, nheads] fp32 output
+ *   dA, dD      [nheads] fp32 outputs (dD also when D is NULL)
+ *   dB, dC      [batch, seqlen, ngroups, dstate] fp32 outputs, summed over
+ *               the heads of each group
+ *   dinit_state [nseq, nheads, headdim, dstate] fp32 output, or NULL
+ *   workspace   >= ssd_chunk_scan_bwd_workspace_size(dims, io_dtype) bytes,
+ *               256-byte aligned, not used by another call in flight (holds
+ *               every chunk-boundary state and state gradient: about
+ *               2 * tokens/64 * nheads * headdim * dstate * 4 bytes).
+ *
+ * Deterministic (fixed reduction orders, no atomics).  Supported: headdim in
+ * {16, 32, 64}, dstate in {16, 32, 64, 128} (bf16) or {16, 32, 64} (fp32).
+ * Outputs must not overlap each other, the inputs or the workspace.
+ */
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims_t *dims, ssd_dtype_t io_dtype);
+
+ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
+                                const void *x, const float *dt, const float *A,
+                                const void *B, const void *C, const float *D,
+                                const float *init_state, const int32_t *cu_seqlens,
+                                const void *dy, const float *dfinal_state,
+                                void *dx, float *ddt, float *dA, float *dB, float *dC,
+                                float *dD, float *dinit_state,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

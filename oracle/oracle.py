@@ -251,13 +251,15 @@ def gated_rmsnorm(y, z, weight, eps: float, group_size=None, norm_before_gate: b
 # differentiation of the forward above, pinned against finite differences of
 # the C oracle in the tests.
 
-def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal=None):
+def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal=None, unit_mask=None):
     """fp64 gradients of L = <dy, y> + <dfinal, final_state> for y, final_state
     = ssd_fwd(x, dt, A, B, C, D, init_state, cu_seqlens).
 
     Shapes as for ssd_fwd; dy like y, dfinal like final_state (or None).
     Returns a dict with dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC
-    [b, L, G, N], dD [H] and dinit [nseq, H, P, N]."""
+    [b, L, G, N], dD [H] and dinit [nseq, H, P, N].  ``unit_mask`` [nseq, H]
+    (bool) restricts the work to some (sequence, head) pairs: the other pairs'
+    gradients stay zero, and dB, dC, dA, dD sum the chosen pairs only."""
     x = _f64(x); dt = _f64(dt); A = _f64(A); B = _f64(B); C = _f64(C); dy = _f64(dy)
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -276,6 +278,8 @@ def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal
                dC=np.zeros_like(C), dD=np.zeros(H), dinit=np.zeros((nseq, H, P, N)))
     for s, (bi, a, e) in enumerate(spans):
         for h in range(H):
+            if unit_mask is not None and not unit_mask[s][h]:
+                continue
             g_ = h // hpg
             # forward, keeping every state
             hs = np.zeros((e - a + 1, P, N))

@@ -12,6 +12,7 @@
 #include "ssd_device.h"
 #include "ssd_fwd_kernel.h"
 #include "ssd_block_kernels.h"
+#include "ssd_bwd_kernels.h"
 
 namespace ssd {
 bool fwd_dispatch_bf16(int p, int n, int q, const FwdParams &prm, long long max_entries, hipStream_t st,
@@ -280,6 +281,44 @@ static bool conv_launch(int width, const ConvParams &p, dim3 grid, hipStream_t s
     case 4: hipLaunchKernelGGL((ssd_conv1d_kernel<IO, 4>), grid, dim3(256), 0, st, p); return true;
     default: return false;
     }
+}
+
+// Backward: headdim 16..64 with dstate 16..128 (bf16) or 16..64 (fp32), where
+// the chunk kernel's tiles fit in LDS.
+template <typename IO, int P, int N>
+static bool bwd_try(int pp, int nn, const BwdParams &p, unsigned units, unsigned n_chunks_max, bool launch,
+                    hipStream_t st) {
+    if (pp != P || nn != N) return false;
+    if (launch) {
+        hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 0>), dim3(units), dim3(256), 0, st, p);
+        hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 1>), dim3(units), dim3(256), 0, st, p);
+        hipLaunchKernelGGL((ssd_bwd_chunk_kernel<IO, P, N>), dim3(n_chunks_max * (unsigned)p.G), dim3(256), 0,
+                           st, p);
+    }
+    return true;
+}
+
+template <typename IO, int P>
+static bool bwd_try_n(int pp, int nn, const BwdParams &p, unsigned units, unsigned ncm, bool launch,
+                      hipStream_t st) {
+    if constexpr (sizeof(IO) == 2) {
+        return bwd_try<IO, P, 16>(pp, nn, p, units, ncm, launch, st) ||
+               bwd_try<IO, P, 32>(pp, nn, p, units, ncm, launch, st) ||
+               bwd_try<IO, P, 64>(pp, nn, p, units, ncm, launch, st) ||
+               bwd_try<IO, P, 128>(pp, nn, p, units, ncm, launch, st);
+    } else {
+        return bwd_try<IO, P, 16>(pp, nn, p, units, ncm, launch, st) ||
+               bwd_try<IO, P, 32>(pp, nn, p, units, ncm, launch, st) ||
+               bwd_try<IO, P, 64>(pp, nn, p, units, ncm, launch, st);
+    }
+}
+
+template <typename IO>
+static bool bwd_dispatch(int pp, int nn, const BwdParams &p, unsigned units, unsigned ncm, bool launch,
+                         hipStream_t st) {
+    return bwd_try_n<IO, 16>(pp, nn, p, units, ncm, launch, st) ||
+           bwd_try_n<IO, 32>(pp, nn, p, units, ncm, launch, st) ||
+           bwd_try_n<IO, 64>(pp, nn, p, units, ncm, launch, st);
 }
 
 template <typename IO, int NCH>
@@ -752,6 +791,141 @@ ssd_status_t ssd_gated_rmsnorm_fwd(int64_t rows, int32_t dim, int32_t group_size
     const bool ok = (io == SSD_BF16) ? ssd::norm_launch<ssd::bf16>(nch, mode, p, blocks, st)
                                      : ssd::norm_launch<float>(nch, mode, p, blocks, st);
     if (!ok) return SSD_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+namespace {
+struct BwdWs {
+    size_t chunks, seqstart, states, radj, partA, partD, total;
+    long long max_chunks;
+};
+
+bool bwd_ws(const ssd_dims_t &d, bool varlen, BwdWs *w) {
+    const long long Q = ssd::kBwdQ;
+    const long long per = (d.seqlen + Q - 1) / Q;
+    w->max_chunks = varlen ? per + d.nseq : per * d.batch;
+    const long long st = (long long)d.nheads * d.headdim * d.dstate * 4;
+    w->chunks = 0;
+    w->seqstart = align_up((size_t)w->max_chunks * 16, 256);
+    w->states = align_up(w->seqstart + (size_t)(d.nseq + 1) * 4, 256);
+    w->radj = align_up(w->states + (size_t)(w->max_chunks + d.nseq) * st, 256);
+    w->partA = align_up(w->radj + (size_t)w->max_chunks * st, 256);
+    w->partD = align_up(w->partA + (size_t)w->max_chunks * d.nheads * 4, 256);
+    w->total = align_up(w->partD + (size_t)w->max_chunks * d.nheads * 4, 256);
+    return true;
+}
+
+ssd_status_t bwd_shape_check(const ssd_dims_t *dims, ssd_dtype_t io, bool varlen) {
+    if (!dims) return SSD_ERR_NULL_PTR;
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
+    const ssd_dims_t &d = *dims;
+    if (!dims_ok(d)) return SSD_ERR_SHAPE;
+    if (varlen ? (d.batch != 1 || d.nseq > 65536) : d.nseq != d.batch) return SSD_ERR_SHAPE;
+    ssd::BwdParams dummy{};
+    const bool built = (io == SSD_BF16) ? ssd::bwd_dispatch<ssd::bf16>(d.headdim, d.dstate, dummy, 0, 0, false, nullptr)
+                                        : ssd::bwd_dispatch<float>(d.headdim, d.dstate, dummy, 0, 0, false, nullptr);
+    if (!built) return SSD_ERR_UNSUPPORTED;
+    if ((long long)d.batch * d.seqlen > INT_MAX / 2 || (long long)d.nseq * d.nheads > INT_MAX) return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+}  // namespace
+
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims_t *dims, ssd_dtype_t io) {
+    if (!dims) return 0;
+    if (bwd_shape_check(dims, io, true) != SSD_OK && bwd_shape_check(dims, io, false) != SSD_OK) return 0;
+    BwdWs a{}, b{};
+    bwd_ws(*dims, true, &a);
+    bwd_ws(*dims, false, &b);
+    return a.total > b.total ? a.total : b.total;
+}
+
+ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const void *x, const float *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *init_state, const int32_t *cu_seqlens, const void *dy,
+                                const float *dfinal_state, void *dx, float *ddt, float *dA, float *dB, float *dC,
+                                float *dD, float *dinit_state, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    const bool varlen = cu_seqlens != nullptr;
+    ssd_status_t st = bwd_shape_check(dims, io, varlen);
+    if (st != SSD_OK) return st;
+    const ssd_dims_t &d = *dims;
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !dD) return SSD_ERR_NULL_PTR;
+    if (!workspace) return SSD_ERR_WORKSPACE;
+    const void *al16[] = {x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA, dB, dC, dD, dinit_state};
+    for (const void *q : al16)
+        if (q && !aligned(q, 16)) return SSD_ERR_ALIGNMENT;
+    if (!aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
+    BwdWs w{};
+    bwd_ws(d, varlen, &w);
+    if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+
+    const size_t E = (io == SSD_BF16) ? 2 : 4;
+    const size_t tokens = (size_t)d.batch * d.seqlen;
+    const size_t nx = tokens * d.nheads * d.headdim, nbc = tokens * d.ngroups * d.dstate;
+    const size_t nst = (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4;
+    const Range ins[] = {rng(x, nx * E), rng(dt, tokens * d.nheads * 4), rng(A, (size_t)d.nheads * 4),
+                         rng(B, nbc * E), rng(C, nbc * E), rng(D, D ? (size_t)d.nheads * 4 : 0),
+                         rng(init_state, init_state ? nst : 0), rng(dy, nx * E),
+                         rng(dfinal_state, dfinal_state ? nst : 0),
+                         rng(cu_seqlens, varlen ? (size_t)(d.nseq + 1) * 4 : 0), rng(workspace, w.total)};
+    const Range outs[] = {rng(dx, nx * E), rng(ddt, tokens * d.nheads * 4), rng(dA, (size_t)d.nheads * 4),
+                          rng(dB, nbc * 4), rng(dC, nbc * 4), rng(dD, (size_t)d.nheads * 4),
+                          rng(dinit_state, dinit_state ? nst : 0)};
+    for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+        for (const Range &r : ins)
+            if (overlap(outs[a], r)) return SSD_ERR_ALIAS;
+        for (size_t b = a + 1; b < sizeof(outs) / sizeof(outs[0]); ++b)
+            if (overlap(outs[a], outs[b])) return SSD_ERR_ALIAS;
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ssd::BwdPrepParams pp{};
+    pp.cu_seqlens = cu_seqlens;
+    pp.batch = d.batch;
+    pp.seqlen = d.seqlen;
+    pp.nseq = d.nseq;
+    pp.seq_chunk_start = reinterpret_cast<int *>(ws + w.seqstart);
+    pp.chunks = reinterpret_cast<int4 *>(ws + w.chunks);
+    hipLaunchKernelGGL(ssd::ssd_bwd_prep_kernel, dim3(1), dim3(256), 0, s, pp);
+
+    ssd::BwdParams p{};
+    p.x = x;
+    p.B = B;
+    p.C = C;
+    p.dy = dy;
+    p.dt = dt;
+    p.A = A;
+    p.D = D;
+    p.init_state = init_state;
+    p.dfinal = dfinal_state;
+    p.dx = dx;
+    p.ddt = ddt;
+    p.dB = dB;
+    p.dC = dC;
+    p.dinit = dinit_state;
+    p.dA = dA;
+    p.dD = dD;
+    p.chunks = pp.chunks;
+    p.seq_chunk_start = pp.seq_chunk_start;
+    p.states = reinterpret_cast<float *>(ws + w.states);
+    p.radj = reinterpret_cast<float *>(ws + w.radj);
+    p.partA = reinterpret_cast<float *>(ws + w.partA);
+    p.partD = reinterpret_cast<float *>(ws + w.partD);
+    p.H = d.nheads;
+    p.G = d.ngroups;
+    p.nseq = d.nseq;
+    const unsigned units = (unsigned)d.nseq * (unsigned)d.nheads;
+    const bool ok = (io == SSD_BF16)
+                        ? ssd::bwd_dispatch<ssd::bf16>(d.headdim, d.dstate, p, units, (unsigned)w.max_chunks, true, s)
+                        : ssd::bwd_dispatch<float>(d.headdim, d.dstate, p, units, (unsigned)w.max_chunks, true, s);
+    if (!ok) return SSD_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(ssd::ssd_bwd_reduce_kernel, dim3((d.nheads + 255) / 256), dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }

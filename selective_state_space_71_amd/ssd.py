@@ -104,6 +104,10 @@ def load_library(path: str = LIB_PATH):
         ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP,
         _VP, _VP, _VP, _VP, _VP,
     ]
+    lib.ssd_chunk_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.c_int]
+    lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
+    lib.ssd_chunk_scan_bwd.argtypes = [ctypes.POINTER(SsdDims), ctypes.c_int] + [_VP] * 18 + [ctypes.c_size_t, _VP]
     lib.ssd_gated_rmsnorm_fwd.restype = ctypes.c_int
     lib.ssd_gated_rmsnorm_fwd.argtypes = [
         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _VP, _VP, _VP, ctypes.c_float,
@@ -332,4 +336,50 @@ def gated_rmsnorm_fwd(y, z, weight, eps: float = 1e-5, group_size=None, norm_bef
                                      1 if norm_before_gate else 0, _ptr(out), _stream(dev))
     if code != 0:
         raise SsdError(code, "ssd_gated_rmsnorm_fwd")
+    return out
+
+
+def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal_state=None,
+                   want_dinit: bool = True, workspace=None):
+    """Backward of ``chunk_scan_fwd`` through ``ssd_chunk_scan_bwd``: gradients
+    of <dy, y> + <dfinal_state, final_state>.  Returns a dict with dx (io
+    dtype), ddt, dA, dB, dC, dD and dinit (fp32; dinit None unless wanted)."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    io = _io_code(x)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _need(dt, "dt", torch.float32, (b, L, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(B, "B", x.dtype, (b, L, G, N), dev)
+    _need(C, "C", x.dtype, (b, L, G, N), dev)
+    _need(dy, "dy", x.dtype, (b, L, H, P), dev)
+    if D is not None:
+        _need(D, "D", torch.float32, (H,), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    dims = fwd_dims(x, B, cu_seqlens)
+    nseq = dims.nseq
+    for name, t in (("init_state", init_state), ("dfinal_state", dfinal_state)):
+        if t is not None:
+            _need(t, name, torch.float32, (nseq, H, P, N), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty((b, L, H), **f32), dA=torch.empty(H, **f32),
+               dB=torch.empty((b, L, G, N), **f32), dC=torch.empty((b, L, G, N), **f32),
+               dD=torch.empty(H, **f32), dinit=torch.empty((nseq, H, P, N), **f32) if want_dinit else None)
+    n = int(lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(dims), io))
+    if n == 0:
+        code = lib.ssd_chunk_scan_bwd(ctypes.byref(dims), io, *([None] * 18), 0, None)
+        raise SsdError(code, "ssd_chunk_scan_bwd (size query)")
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    code = lib.ssd_chunk_scan_bwd(ctypes.byref(dims), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(init_state), _ptr(cu_seqlens), _ptr(dy), _ptr(dfinal_state),
+                                  _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                                  _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel()), _stream(dev))
+    if code != 0:
+        raise SsdError(code, "ssd_chunk_scan_bwd")
+    chunk_scan_bwd.last_workspace = workspace
     return out

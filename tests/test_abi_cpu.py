@@ -25,7 +25,7 @@ def test_header_symbols_are_exported(lib):
     assert {"ssd_chunk_scan_fwd", "ssd_decode_step", "ssd_chunk_scan_fwd_workspace_size",
             "ssd_status_string", "ssd_abi_version", "ssd_chunk_scan_fwd_check",
             "ssd_chunk_scan_fwd_ex", "ssd_decode_step_ex", "ssd_causal_conv1d_fwd",
-            "ssd_gated_rmsnorm_fwd"} <= set(names)
+            "ssd_gated_rmsnorm_fwd", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -35,7 +35,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 3
+    assert lib.ssd_abi_version() == 4
     for code, name in ssd._STATUS.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(77)
@@ -219,6 +219,49 @@ def _norm(lib, rows=16, dim=5120, gs=5120, io=ssd.SSD_BF16, eps=1e-5, **ptrs):
 ])
 def test_norm_validation_rejects(lib, case, expect):
     assert _norm(lib, **case) == expect
+
+
+
+def _bwd(lib, dims, io=ssd.SSD_BF16, **ptrs):
+    base = FAKE
+    names = ["x", "dt", "A", "B", "C", "D", "init", "cu", "dy", "dfin", "dx", "ddt", "dA", "dB", "dC", "dD",
+             "dinit"]
+    dp = {n: base + ((i + 1) << 34) for i, n in enumerate(names)}
+    for n in ("D", "init", "cu", "dfin", "dinit"):
+        dp[n] = None
+    dp.update(ws=FAKE + (40 << 34), wsb=1 << 40)
+    dp.update(ptrs)
+    return lib.ssd_chunk_scan_bwd(ctypes.byref(dims) if dims is not None else None, io,
+                                  *[dp[n] for n in names], dp["ws"], ctypes.c_size_t(dp["wsb"]), None)
+
+
+def test_bwd_workspace_size_query(lib):
+    n = lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims()), ssd.SSD_BF16)
+    # every boundary state and state gradient of 512/64 chunks x 2 sequences x 8 heads
+    assert n >= 2 * 2 * 8 * 8 * 64 * 128 * 4 and n % 256 == 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(headdim=128)), ssd.SSD_BF16) == 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=128)), ssd.SSD_F32) == 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=64)), ssd.SSD_F32) > 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), 1),
+    (dict(io=7), 3),
+    (dict(dims=_dims(headdim=128)), 4),
+    (dict(dims=_dims(dstate=256)), 4),
+    (dict(dims=_dims(nseq=3)), 2),
+    (dict(dy=None), 1),
+    (dict(dB=None), 1),
+    (dict(ws=None), 7),
+    (dict(wsb=4096), 7),
+    (dict(dx=FAKE + (11 << 34) + 8), 5),
+    (dict(dx=FAKE + (9 << 34)), 6),                              # dx over dy
+    (dict(dC=FAKE + (14 << 34) + 64), 6),                        # dC over dB
+    (dict(ddt=FAKE + (40 << 34) + 256), 6),                      # ddt inside the workspace
+])
+def test_bwd_validation_rejects(lib, case, expect):
+    dims = case.pop("dims", _dims())
+    assert _bwd(lib, dims, **case) == expect
 
 
 # (last: it reloads the binding module, which redefines its ctypes structures)
