@@ -290,10 +290,19 @@ static bool bwd_try(int pp, int nn, const BwdParams &p, unsigned units, unsigned
                     hipStream_t st) {
     if (pp != P || nn != N) return false;
     if (launch) {
-        hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 0>), dim3(units), dim3(256), 0, st, p);
-        hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 1>), dim3(units), dim3(256), 0, st, p);
-        hipLaunchKernelGGL((ssd_bwd_chunk_kernel<IO, P, N>), dim3(n_chunks_max * (unsigned)p.G), dim3(256), 0,
-                           st, p);
+        if constexpr (sizeof(IO) == 2 && P >= 32 && N >= 32) {
+            hipLaunchKernelGGL((ssd_bwd_scan_bf16_kernel<P, N, 0>), dim3(units), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((ssd_bwd_scan_bf16_kernel<P, N, 1>), dim3(units), dim3(256), 0, st, p);
+        } else {
+            hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 0>), dim3(units), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 1>), dim3(units), dim3(256), 0, st, p);
+        }
+        if constexpr (sizeof(IO) == 2 && P >= 32 && N >= 32)
+            hipLaunchKernelGGL((ssd_bwd_chunk_bf16_kernel<P, N>), dim3(n_chunks_max * (unsigned)p.G), dim3(256), 0,
+                               st, p);
+        else
+            hipLaunchKernelGGL((ssd_bwd_chunk_kernel<IO, P, N>), dim3(n_chunks_max * (unsigned)p.G), dim3(256), 0,
+                               st, p);
     }
     return true;
 }
@@ -925,7 +934,7 @@ ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const vo
                         ? ssd::bwd_dispatch<ssd::bf16>(d.headdim, d.dstate, p, units, (unsigned)w.max_chunks, true, s)
                         : ssd::bwd_dispatch<float>(d.headdim, d.dstate, p, units, (unsigned)w.max_chunks, true, s);
     if (!ok) return SSD_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(ssd::ssd_bwd_reduce_kernel, dim3((d.nheads + 255) / 256), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ssd::ssd_bwd_reduce_kernel, dim3(d.nheads), dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }

@@ -473,18 +473,417 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
         }
 }
 
-// dA[h], dD[h]: sums of the per-chunk partials in chunk order.
+// ---------------------------------------------------------------------------
+// bf16 version of the chunk kernel for headdim and dstate >= 32: every MFMA
+// operand is read from LDS in the K-slot order of the forward kernel (slot e
+// of lane group lg holds k0 + 16 (e / 4) + 4 lg + e % 4): two 8-byte reads for
+// an operand whose K index runs along its rows, or two transposing reads when
+// it runs down its columns.  Per head, C B^T and dY X^T are formed in
+// registers (a 16-row band per wave); the decayed, masked M and W go to LDS
+// once, and the row/column sums of their product come from the same
+// registers.  H and R are kept as split bf16 pairs.
+template <int S>
+__device__ __forceinline__ bf16x8 frag_row(const bf16 *base, int m, int k0, int lg) {
+    const bf16 *q = base + m * S + k0 + 4 * lg;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(q);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(q + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int S>
+__device__ __forceinline__ bf16x8 frag_col(const bf16 *base, int k0, int n0, int li, int lg) {
+    const int row = k0 + 4 * lg + (li >> 2);
+    const int col = n0 + 4 * (li & 3);
+    const bf16x4 lo = lds_read_tr16(base + row * S + col);
+    const bf16x4 hi = lds_read_tr16(base + (row + 16) * S + col);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(f32x4 acc, bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+template <int P, int N>
+__global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
+    constexpr int Q = kBwdQ;
+    constexpr int NT = N / 16, PT = P / 16;
+    constexpr int SP = P + 8, SN = N + 8, SQ = Q + 8;   // padded row strides (elements)
+    __shared__ __attribute__((aligned(16))) bf16 xs[Q * SP];
+    __shared__ __attribute__((aligned(16))) bf16 dys[Q * SP];
+    __shared__ __attribute__((aligned(16))) bf16 Bs[Q * SN];
+    __shared__ __attribute__((aligned(16))) bf16 Cs[Q * SN];
+    __shared__ __attribute__((aligned(16))) bf16 Ms[Q * SQ];
+    __shared__ __attribute__((aligned(16))) bf16 Ws[Q * SQ];
+    __shared__ __attribute__((aligned(16))) bf16 Hh[P * SN];
+    __shared__ __attribute__((aligned(16))) bf16 Hl[P * SN];
+    __shared__ __attribute__((aligned(16))) bf16 Rh[P * SN];
+    __shared__ __attribute__((aligned(16))) bf16 Rl[P * SN];
+    __shared__ float s2[Q], dtv[Q], ew[Q], es[Q];
+    __shared__ float rowZ[Q], colP[4][Q], offB[Q], offC[Q];
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int ci = blockIdx.x / p.G, g = blockIdx.x - ci * p.G;
+    if (ci >= p.seq_chunk_start[p.nseq]) return;
+    const int4 ce = p.chunks[ci];
+    const int s = ce.x, c = ce.w, q = ce.z;
+    const long long t0 = ce.y;
+    const int o = p.seq_chunk_start[s];
+    const int H = p.H, hpg = H / p.G;
+    const long long PN = (long long)P * N;
+    const int row0 = wave * 16;
+
+    auto stage = [&](bf16 *dst, const bf16 *src, int W, int SW, long long stride, long long col) {
+        const int V8 = W / 8;
+        for (int i = tid; i < Q * V8; i += 256) {
+            const int j = i / V8, c8 = (i - j * V8) * 8;
+            bf16x8 v = zero_frag<bf16x8>();
+            if (j < q) v = *reinterpret_cast<const bf16x8 *>(src + (t0 + j) * stride + col + c8);
+            *reinterpret_cast<bf16x8 *>(dst + j * SW + c8) = v;
+        }
+    };
+    const bf16 *Bg = reinterpret_cast<const bf16 *>(p.B), *Cg = reinterpret_cast<const bf16 *>(p.C);
+    stage(Bs, Bg, N, SN, (long long)p.G * N, (long long)g * N);
+    stage(Cs, Cg, N, SN, (long long)p.G * N, (long long)g * N);
+
+    f32x4 dBacc[NT], dCacc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dBacc[nt] = dCacc[nt] = zero4();
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        __syncthreads();   // the previous head's tiles are no longer read
+        const bf16 *xg = reinterpret_cast<const bf16 *>(p.x), *dyg = reinterpret_cast<const bf16 *>(p.dy);
+        stage(xs, xg, P, SP, (long long)H * P, (long long)h * P);
+        stage(dys, dyg, P, SP, (long long)H * P, (long long)h * P);
+        const float *Hc = p.states + ((long long)(o + s + c) * H + h) * PN;
+        const float *Hn = p.states + ((long long)(o + s + c + 1) * H + h) * PN;
+        const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
+        float rh = 0.f;
+        for (int i = tid * 4; i < P * N; i += 256 * 4) {
+            const f32x4 hv = *reinterpret_cast<const f32x4 *>(Hc + i);
+            const f32x4 rv = *reinterpret_cast<const f32x4 *>(Rc + i);
+            const f32x4 nv = *reinterpret_cast<const f32x4 *>(Hn + i);
+            const int pp = i / N, nn = i - pp * N;
+            bf16x4 a, b, cc, d;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = (bf16)hv[e];
+                b[e] = (bf16)(hv[e] - (float)a[e]);
+                cc[e] = (bf16)rv[e];
+                d[e] = (bf16)(rv[e] - (float)cc[e]);
+                rh += rv[e] * nv[e];
+            }
+            *reinterpret_cast<bf16x4 *>(Hh + pp * SN + nn) = a;
+            *reinterpret_cast<bf16x4 *>(Hl + pp * SN + nn) = b;
+            *reinterpret_cast<bf16x4 *>(Rh + pp * SN + nn) = cc;
+            *reinterpret_cast<bf16x4 *>(Rl + pp * SN + nn) = d;
+        }
+        const float Ah = p.A[h];
+        if (wave == 0) {
+            const float d = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
+            const float sc = bwd_wave_scan(d * Ah, lane) * kBwdLog2e;
+            const float slast = __shfl(sc, 63, 64);
+            s2[lane] = sc;
+            dtv[lane] = d;
+            ew[lane] = __builtin_amdgcn_exp2f(slast - sc);
+            es[lane] = __builtin_amdgcn_exp2f(sc);
+        }
+        rh = block_sum(rh, red);   // (its barriers also publish the tiles above)
+
+        // C B^T and dY X^T for rows row0..row0+15, then M, W and the Z sums
+        {
+            f32x4 gt[4], et[4];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                gt[jt] = et[jt] = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += 32)
+                    gt[jt] = mfma_bf16(gt[jt], frag_row<SN>(Cs, row0 + li, k0, lg), frag_row<SN>(Bs, jt * 16 + li, k0, lg));
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += 32)
+                    et[jt] = mfma_bf16(et[jt], frag_row<SP>(dys, row0 + li, k0, lg), frag_row<SP>(xs, jt * 16 + li, k0, lg));
+            }
+            float rz[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                const int j = jt * 16 + li;
+                const float sj = s2[j], dj = dtv[j];
+                float cz = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = row0 + 4 * lg + r;
+                    const float dec = j <= i ? __builtin_amdgcn_exp2f(s2[i] - sj) : 0.f;
+                    const float z = gt[jt][r] * et[jt][r] * dec;
+                    rz[r] += z * dj;
+                    cz += z;
+                    Ms[i * SQ + j] = (bf16)(gt[jt][r] * dec * dj);
+                    Ws[i * SQ + j] = (bf16)(et[jt][r] * dec * dj);
+                }
+                cz += __shfl_xor(cz, 16, 64);
+                cz += __shfl_xor(cz, 32, 64);
+                if (lg == 0) colP[wave][j] = cz;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) rz[r] += __shfl_xor(rz[r], m, 64);
+                if (li == 0) rowZ[row0 + 4 * lg + r] = rz[r];
+            }
+        }
+        float dd = 0.f;   // dy . x over the chunk
+        for (int i = tid; i < Q * P; i += 256) {
+            const int j = i / P, pp = i - j * P;
+            dd += (float)dys[j * SP + pp] * (float)xs[j * SP + pp];
+        }
+        dd = block_sum(dd, red);   // (also publishes M and W)
+        if (tid == 0) p.partD[(long long)ci * H + h] = dd;
+
+        // dx = M^T dY + diag(w) B R^T + D dY
+        const float Dh = p.D ? p.D[h] : 0.f;
+        bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < Q; k0 += 32)
+                a1 = mfma_bf16(a1, frag_col<SQ>(Ms, k0, row0, li, lg), frag_col<SP>(dys, k0, pt * 16, li, lg));
+#pragma unroll
+            for (int k0 = 0; k0 < N; k0 += 32)
+                a2 = mfma_bf16(a2, frag_row<SN>(Bs, row0 + li, k0, lg), frag_row<SN>(Rh, pt * 16 + li, k0, lg));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = row0 + 4 * lg + r, pp = pt * 16 + li;
+                if (j < q)
+                    dxg[((t0 + j) * H + h) * P + pp] =
+                        (bf16)(a1[r] + ew[j] * dtv[j] * a2[r] + Dh * (float)dys[j * SP + pp]);
+            }
+        }
+
+        // dB, dC of this head and the row dot products of their low-rank parts
+        float ob[4] = {0.f, 0.f, 0.f, 0.f}, oc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 db = zero4(), dc = zero4(), xb = zero4(), yc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < Q; k0 += 32) {
+                db = mfma_bf16(db, frag_col<SQ>(Ws, k0, row0, li, lg), frag_col<SN>(Cs, k0, nt * 16, li, lg));
+                const bf16x8 bcol = frag_col<SN>(Bs, k0, nt * 16, li, lg);
+                dc = mfma_bf16(dc, frag_row<SQ>(Ws, row0 + li, k0, lg), bcol);
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < P; k0 += 32) {
+                const bf16x8 xr = frag_row<SP>(xs, row0 + li, k0, lg);
+                xb = mfma_bf16(xb, xr, frag_col<SN>(Rh, k0, nt * 16, li, lg));
+                xb = mfma_bf16(xb, xr, frag_col<SN>(Rl, k0, nt * 16, li, lg));
+                const bf16x8 yr = frag_row<SP>(dys, row0 + li, k0, lg);
+                yc = mfma_bf16(yc, yr, frag_col<SN>(Hh, k0, nt * 16, li, lg));
+                yc = mfma_bf16(yc, yr, frag_col<SN>(Hl, k0, nt * 16, li, lg));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rr = row0 + 4 * lg + r, nn = nt * 16 + li;
+                const float xbr = xb[r] * ew[rr], ycr = yc[r] * es[rr];
+                dBacc[nt][r] += db[r] + dtv[rr] * xbr;
+                dCacc[nt][r] += dc[r] + ycr;
+                ob[r] += xbr * (float)Bs[rr * SN + nn];
+                oc[r] += ycr * (float)Cs[rr * SN + nn];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                ob[r] += __shfl_xor(ob[r], m, 64);
+                oc[r] += __shfl_xor(oc[r], m, 64);
+            }
+            if (li == 0) {
+                offB[row0 + 4 * lg + r] = ob[r];
+                offC[row0 + 4 * lg + r] = oc[r];
+            }
+        }
+        __syncthreads();
+
+        if (wave == 0) {
+            const int j = lane;
+            const float d = dtv[j];
+            const float cz = colP[0][j] + colP[1][j] + colP[2][j] + colP[3][j];
+            const float ds = rowZ[j] - d * cz + offC[j] - d * offB[j] + (j == q - 1 ? rh : 0.f);
+            const float tot = bwd_wave_sum(ds);
+            const float da = tot - bwd_wave_scan(ds, lane) + ds;
+            if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + cz + offB[j];
+            const float pa = bwd_wave_sum(d * da);
+            if (lane == 0) p.partA[(long long)ci * H + h] = pa;
+        }
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = row0 + 4 * lg + r, nn = nt * 16 + li;
+            if (rr < q) {
+                p.dB[((t0 + rr) * p.G + g) * N + nn] = dBacc[nt][r];
+                p.dC[((t0 + rr) * p.G + g) * N + nn] = dCacc[nt][r];
+            }
+        }
+}
+
+// bf16 version of the chunk-sequential scan for headdim and dstate >= 32.  The
+// next chunk's rows and dt are loaded into registers while the current chunk
+// is computed; u is scaled by the decay weights once per chunk and kept in LDS
+// as a split bf16 pair, and both MFMA operands are read in the K-slot order
+// with transposing LDS reads.
+template <int P, int N, int MODE>
+__global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
+    constexpr int Q = kBwdQ;
+    constexpr int PT = P / 16, NT = N / 16, TILES = PT * NT;
+    constexpr int TPW = (TILES + 3) / 4;
+    constexpr int SP = P + 8, SN = N + 8;
+    constexpr int UV = Q * P / 8 / 256;     // 16-byte pieces of u per thread (P >= 32: 1 or 2)
+    constexpr int VV = Q * N / 8 / 256;     // likewise for v (1, 2 or 4)
+    static_assert(UV >= 1 && VV >= 1, "shape too small for this kernel");
+    __shared__ __attribute__((aligned(16))) bf16 sv[Q * SN];
+    __shared__ __attribute__((aligned(16))) bf16 uh[Q * SP];
+    __shared__ __attribute__((aligned(16))) bf16 ul[Q * SP];
+    __shared__ float swt[Q];
+    __shared__ float salpha;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int s = blockIdx.x / p.H, h = blockIdx.x - s * p.H;
+    const int g = h / (p.H / p.G);
+    const int o = p.seq_chunk_start[s];
+    const int nc = p.seq_chunk_start[s + 1] - o;
+    const long long PN = (long long)P * N;
+    const bf16 *ug = reinterpret_cast<const bf16 *>(MODE == 0 ? p.x : p.dy);
+    const bf16 *vg = reinterpret_cast<const bf16 *>(MODE == 0 ? p.B : p.C);
+    const float Ah = p.A[h];
+
+    f32x4 st[TPW];
+    const float *st0 = MODE == 0 ? p.init_state : p.dfinal;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int t = wave + 4 * k;
+        st[k] = zero4();
+        if (t < TILES && st0) {
+            const int pp = (t % PT) * 16 + li, nn = (t / PT) * 16 + 4 * lg;
+            st[k] = *reinterpret_cast<const f32x4 *>(st0 + ((long long)s * p.H + h) * PN + pp * N + nn);
+        }
+    }
+    auto store_state = [&](float *dst) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int t = wave + 4 * k;
+            if (t < TILES) {
+                const int pp = (t % PT) * 16 + li, nn = (t / PT) * 16 + 4 * lg;
+                *reinterpret_cast<f32x4 *>(dst + pp * N + nn) = st[k];
+            }
+        }
+    };
+    if (MODE == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
+
+    // registers of one chunk: u and v pieces (row j, 8 columns) and dt (wave 0)
+    bf16x8 ur[UV], vr[VV];
+    float dtr = 0.f;
+    auto load_chunk = [&](int c) {
+        const int4 ce = p.chunks[o + c];
+        const long long t0 = ce.y;
+        const int q = ce.z;
+#pragma unroll
+        for (int k = 0; k < UV; ++k) {
+            const int i = tid + 256 * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
+            ur[k] = zero_frag<bf16x8>();
+            if (j < q) ur[k] = *reinterpret_cast<const bf16x8 *>(ug + ((t0 + j) * p.H + h) * P + c8);
+        }
+#pragma unroll
+        for (int k = 0; k < VV; ++k) {
+            const int i = tid + 256 * k, j = i / (N / 8), c8 = (i % (N / 8)) * 8;
+            vr[k] = zero_frag<bf16x8>();
+            if (j < q) vr[k] = *reinterpret_cast<const bf16x8 *>(vg + ((t0 + j) * p.G + g) * N + c8);
+        }
+        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * p.H + h] : 0.f;
+    };
+    if (nc > 0) load_chunk(MODE == 0 ? 0 : nc - 1);
+
+    for (int step = 0; step < nc; ++step) {
+        const int c = MODE == 0 ? step : nc - 1 - step;
+        // v rows and the weights of this chunk into LDS
+#pragma unroll
+        for (int k = 0; k < VV; ++k) {
+            const int i = tid + 256 * k, j = i / (N / 8), c8 = (i % (N / 8)) * 8;
+            *reinterpret_cast<bf16x8 *>(sv + j * SN + c8) = vr[k];
+        }
+        if (wave == 0) {
+            const float sc = bwd_wave_scan(dtr * Ah, lane) * kBwdLog2e;
+            const float slast = __shfl(sc, 63, 64);
+            swt[lane] = MODE == 0 ? __builtin_amdgcn_exp2f(slast - sc) * dtr : __builtin_amdgcn_exp2f(sc);
+            if (lane == 0) salpha = __builtin_amdgcn_exp2f(slast);
+        }
+        __syncthreads();
+        // u scaled by the weights, as a split pair
+#pragma unroll
+        for (int k = 0; k < UV; ++k) {
+            const int i = tid + 256 * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
+            const float w = swt[j];
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = (float)ur[k][e] * w;
+                hi[e] = (bf16)v;
+                lo[e] = (bf16)(v - (float)hi[e]);
+            }
+            *reinterpret_cast<bf16x8 *>(uh + j * SP + c8) = hi;
+            *reinterpret_cast<bf16x8 *>(ul + j * SP + c8) = lo;
+        }
+        const float alpha = salpha;
+        __syncthreads();
+        if (step + 1 < nc) load_chunk(MODE == 0 ? c + 1 : c - 1);   // in flight during the MFMAs
+        if (MODE == 1) store_state(p.radj + ((long long)(o + c) * p.H + h) * PN);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int t = wave + 4 * k;
+            if (t < TILES) {
+                const int pt = t % PT, nt = t / PT;
+                // rows n (A operand v^T), columns p (B operand: u scaled by the weights)
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < Q; k0 += 32) {
+                    const bf16x8 a = frag_col<SN>(sv, k0, nt * 16, li, lg);
+                    acc = mfma_bf16(acc, a, frag_col<SP>(uh, k0, pt * 16, li, lg));
+                    acc = mfma_bf16(acc, a, frag_col<SP>(ul, k0, pt * 16, li, lg));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[k][r] = alpha * st[k][r] + acc[r];
+            }
+        }
+        if (MODE == 0) store_state(p.states + ((long long)(o + s + c + 1) * p.H + h) * PN);
+        __syncthreads();   // the LDS tiles are rewritten by the next chunk
+    }
+    if (MODE == 1 && p.dinit) store_state(p.dinit + ((long long)s * p.H + h) * PN);
+}
+
+// dA[h], dD[h]: sums of the per-chunk partials, one workgroup per head, in a
+// fixed order (strided partial sums, then a fixed tree).
 __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdParams p) {
-    const int h = blockIdx.x * 256 + threadIdx.x;
-    if (h >= p.H) return;
+    __shared__ float red[2][4];
+    const int h = blockIdx.x;
     const int n_chunks = p.seq_chunk_start[p.nseq];
     float a = 0.f, d = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
+    for (int c = threadIdx.x; c < n_chunks; c += 256) {
         a += p.partA[(long long)c * p.H + h];
         d += p.partD[(long long)c * p.H + h];
     }
-    p.dA[h] = a;
-    p.dD[h] = d;
+    a = bwd_wave_sum(a);
+    d = bwd_wave_sum(d);
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = a;
+        red[1][threadIdx.x >> 6] = d;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        p.dA[h] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        p.dD[h] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    }
 }
 
 }  // namespace ssd
