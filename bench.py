@@ -14,7 +14,9 @@ per-token figures) and, in "mfma", its algorithmic bf16 MFMA rate.  The
 workload.  A decode line for the b256 H80 P64 N128 single-token step is
 included under "decode", and the block prologue (causal convolution of the
 fused x|B|C projection) and epilogue (gated RMSNorm) at the same 2.7B layer
-shape under "block" (skip with --no-block).
+shape under "block" (skip with --no-block), and the backward pass
+(ssd_chunk_scan_bwd, all gradients) at the forward's workload under
+"backward" (skip with --no-bwd).
 """
 from __future__ import annotations
 
@@ -106,6 +108,46 @@ def bench_block(w, stream, to_dev):
     return res
 
 
+def bwd_algorithmic(w, Qb=64):
+    """Algorithmic bytes and MFMA flops of one backward pass.
+
+    Bytes: read x, dy, dt, B, C, the initial state and the final-state
+    gradient; write dx, ddt, dB and dC (fp32) and the initial-state gradient.
+    Flops per (token, head), with the backward's 64-token chunks: the causal
+    halves of dY X^T, M^T dY, W^T C and W B, 2 Q (P + N); the low-rank terms
+    B R^T, X R and dY H, 6 P N; the two chunk-state contractions of the scans,
+    4 P N.  Per (token, group): the causal half of C B^T, Q N."""
+    b, L, H, P, N, G = w["batch"], w["seqlen"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"]
+    tok = b * L
+    byts = tok * (H * P * 2 * 3 + H * 4 * 2 + G * N * (2 * 2 + 4 * 2)) + 3 * b * H * P * N * 4
+    flops = tok * H * (2 * Qb * (P + N) + 10 * P * N) + tok * G * Qb * N
+    return float(byts), float(flops)
+
+
+def bench_backward(w, stream, x, dt, A, B, C, D, h0):
+    import torch
+    from selective_state_space_71_amd import ssd
+    g = torch.Generator(device=x.device)
+    g.manual_seed(7101)
+    dy = torch.randn(x.shape, generator=g, device=x.device).to(torch.bfloat16)
+    dfin = torch.randn(h0.shape, generator=g, device=x.device)
+    ssd.chunk_scan_bwd(x, dt, A, B, C, dy, D=D, init_state=h0, dfinal_state=dfin)
+    ws = ssd.chunk_scan_bwd.last_workspace
+    us = time_calls(lambda: ssd.chunk_scan_bwd(x, dt, A, B, C, dy, D=D, init_state=h0, dfinal_state=dfin,
+                                               workspace=ws), stream, nrep=10)
+    byts, flops = bwd_algorithmic(w)
+    tok = w["batch"] * w["seqlen"]
+    res = {"workload": "backward of the forward workload above: all gradients (dx bf16; ddt, dA, dB, dC, dD, "
+                       "dinit fp32), 64-token chunks",
+           "us": us, "tokens_per_s": tok / (us * 1e-6),
+           "alg_bytes": byts, "achieved_gbs": byts / (us * 1e-6) / 1e9, "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "alg_flops": flops, "achieved_tflops": flops / (us * 1e-6) / 1e12,
+           "mfma_frac": flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+           "workspace_bytes": int(ws.numel())}
+    del ws
+    return res
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     for f in ("ssd_fwd_kernel.h", "ssd_device.h", "ssd_fwd_launch.h"):
@@ -136,6 +178,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-block", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
@@ -256,6 +299,9 @@ def main():
 
     if not args.no_block:
         out["block"] = bench_block(w, stream, to_dev)
+
+    if not args.no_bwd:
+        out["backward"] = bench_backward(w, stream, x, dt, A, B, C, D, h0)
 
     if not args.no_cpu_baseline:
         from oracle import oracle
