@@ -28,6 +28,8 @@
 // ssd_bwd_reduce_kernel (dA and dD from per-chunk partials, in a fixed order).
 #pragma once
 
+#include <type_traits>
+
 #include "ssd_device.h"
 
 namespace ssd {
@@ -533,18 +535,26 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
     const long long PN = (long long)P * N;
     const int row0 = wave * 16;
 
-    auto stage = [&](bf16 *dst, const bf16 *src, int W, int SW, long long stride, long long col) {
-        const int V8 = W / 8;
-        for (int i = tid; i < Q * V8; i += 256) {
-            const int j = i / V8, c8 = (i - j * V8) * 8;
-            bf16x8 v = zero_frag<bf16x8>();
-            if (j < q) v = *reinterpret_cast<const bf16x8 *>(src + (t0 + j) * stride + col + c8);
-            *reinterpret_cast<bf16x8 *>(dst + j * SW + c8) = v;
+    // rows of a token-major io tensor into a padded LDS tile; all loads first
+    auto stage = [&](auto w_c, bf16 *dst, const bf16 *src, int SW, long long stride, long long col) {
+        constexpr int W = decltype(w_c)::value;
+        constexpr int V8 = W / 8, NV = Q * V8 / 256;
+        bf16x8 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int i = tid + 256 * k, j = i / V8, c8 = (i - j * V8) * 8;
+            v[k] = zero_frag<bf16x8>();
+            if (j < q) v[k] = *reinterpret_cast<const bf16x8 *>(src + (t0 + j) * stride + col + c8);
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int i = tid + 256 * k, j = i / V8, c8 = (i - j * V8) * 8;
+            *reinterpret_cast<bf16x8 *>(dst + j * SW + c8) = v[k];
         }
     };
     const bf16 *Bg = reinterpret_cast<const bf16 *>(p.B), *Cg = reinterpret_cast<const bf16 *>(p.C);
-    stage(Bs, Bg, N, SN, (long long)p.G * N, (long long)g * N);
-    stage(Cs, Cg, N, SN, (long long)p.G * N, (long long)g * N);
+    stage(std::integral_constant<int, N>{}, Bs, Bg, SN, (long long)p.G * N, (long long)g * N);
+    stage(std::integral_constant<int, N>{}, Cs, Cg, SN, (long long)p.G * N, (long long)g * N);
 
     f32x4 dBacc[NT], dCacc[NT];
 #pragma unroll
@@ -554,16 +564,26 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
         const int h = g * hpg + hh;
         __syncthreads();   // the previous head's tiles are no longer read
         const bf16 *xg = reinterpret_cast<const bf16 *>(p.x), *dyg = reinterpret_cast<const bf16 *>(p.dy);
-        stage(xs, xg, P, SP, (long long)H * P, (long long)h * P);
-        stage(dys, dyg, P, SP, (long long)H * P, (long long)h * P);
+        stage(std::integral_constant<int, P>{}, xs, xg, SP, (long long)H * P, (long long)h * P);
+        stage(std::integral_constant<int, P>{}, dys, dyg, SP, (long long)H * P, (long long)h * P);
         const float *Hc = p.states + ((long long)(o + s + c) * H + h) * PN;
         const float *Hn = p.states + ((long long)(o + s + c + 1) * H + h) * PN;
         const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
         float rh = 0.f;
-        for (int i = tid * 4; i < P * N; i += 256 * 4) {
-            const f32x4 hv = *reinterpret_cast<const f32x4 *>(Hc + i);
-            const f32x4 rv = *reinterpret_cast<const f32x4 *>(Rc + i);
-            const f32x4 nv = *reinterpret_cast<const f32x4 *>(Hn + i);
+        // every load of the three state tiles is issued before any is used
+        constexpr int SV = P * N / 1024;   // 4-float pieces per thread
+        f32x4 hvs[SV], rvs[SV], nvs[SV];
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            const int i = (tid + 256 * k) * 4;
+            hvs[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
+            rvs[k] = *reinterpret_cast<const f32x4 *>(Rc + i);
+            nvs[k] = *reinterpret_cast<const f32x4 *>(Hn + i);
+        }
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            const int i = (tid + 256 * k) * 4;
+            const f32x4 hv = hvs[k], rv = rvs[k], nv = nvs[k];
             const int pp = i / N, nn = i - pp * N;
             bf16x4 a, b, cc, d;
 #pragma unroll
