@@ -298,8 +298,8 @@ static bool bwd_try(int pp, int nn, const BwdParams &p, unsigned units, unsigned
             hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 1>), dim3(units), dim3(256), 0, st, p);
         }
         if constexpr (sizeof(IO) == 2 && P >= 32 && N >= 32)
-            hipLaunchKernelGGL((ssd_bwd_chunk_bf16_kernel<P, N>), dim3(n_chunks_max * (unsigned)p.G), dim3(256), 0,
-                               st, p);
+            hipLaunchKernelGGL((ssd_bwd_chunk_bf16_kernel<P, N, kBwdChunkWaves>), dim3(n_chunks_max * (unsigned)p.G),
+                               dim3(64 * kBwdChunkWaves), 0, st, p);
         else
             hipLaunchKernelGGL((ssd_bwd_chunk_kernel<IO, P, N>), dim3(n_chunks_max * (unsigned)p.G), dim3(256), 0,
                                st, p);

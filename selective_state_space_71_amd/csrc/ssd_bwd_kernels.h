@@ -302,14 +302,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
         stage_rows<IO, P>(xs, reinterpret_cast<const IO *>(p.x), t0, q, (long long)H * P, (long long)h * P, tid);
         stage_rows<IO, P>(dys, reinterpret_cast<const IO *>(p.dy), t0, q, (long long)H * P, (long long)h * P, tid);
         const float *Hc = p.states + ((long long)(o + s + c) * H + h) * PN;
-        const float *Hn = p.states + ((long long)(o + s + c + 1) * H + h) * PN;
         const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
-        float rh = 0.f;
+        float hrd = 0.f;   // <R_c, H_c>
         for (int i = tid; i < P * N; i += 256) {
-            const float r = Rc[i];
-            Hs[i] = Hc[i];
-            Rs[i] = r;
-            rh += r * Hn[i];
+            const float hv = Hc[i], rv = Rc[i];
+            Hs[i] = hv;
+            Rs[i] = rv;
+            hrd += hv * rv;
         }
         const float Ah = p.A[h];
         if (wave == 0) {
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
             ew[lane] = __builtin_amdgcn_exp2f(slast - sc);
             es[lane] = __builtin_amdgcn_exp2f(sc);
         }
-        rh = block_sum(rh, red);   // (its barriers also publish the tiles above)
+        hrd = block_sum(hrd, red);   // (its barriers also publish the tiles above)
 
         // E = dY X^T, row band w
 #pragma unroll
@@ -453,6 +452,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
         if (wave == 0) {
             const int j = lane;
             const float d = dtv[j];
+            // <R_c, H_{c+1}> = exp(s_last) <R_c, H_c> + <R_c, S_c>, and <R_c, S_c> = sum_j dt_j offB_j
+            const float rh = __builtin_amdgcn_exp2f(s2[Q - 1]) * hrd + bwd_wave_sum(d * offB[j]);
             float ds = rowZ[j] - d * colZ[j] + offC[j] - d * offB[j] + (j == q - 1 ? rh : 0.f);
             const float tot = bwd_wave_sum(ds);
             const float da = tot - bwd_wave_scan(ds, lane) + ds;    // sum over i >= j
@@ -505,11 +506,19 @@ __device__ __forceinline__ f32x4 mfma_bf16(f32x4 acc, bf16x8 a, bf16x8 b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
-template <int P, int N>
-__global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
+constexpr int kBwdChunkWaves = 8;   // waves per workgroup of the bf16 chunk kernel (4 or 8)
+
+template <int P, int N, int NW>
+__global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
     constexpr int Q = kBwdQ;
     constexpr int NT = N / 16, PT = P / 16;
+    constexpr int NTH = NW * 64;                       // threads
+    constexpr int NH = NW / 4;                         // column parts: waves w and w + 4 share a row band
+    constexpr int NT2 = NT / NH, PT2 = PT / NH;        // tiles per column part
     constexpr int SP = P + 8, SN = N + 8, SQ = Q + 8;   // padded row strides (elements)
+    constexpr int XP = Q * P / 8, SP4 = P * N / 4;     // 16-byte x (dy) pieces, 4-float H (R) pieces
+    constexpr int XV = (XP + NTH - 1) / NTH, SV = (SP4 + NTH - 1) / NTH;   // per thread, rounded up
+    static_assert((NW == 4 || NW == 8) && NT2 >= 1 && PT2 >= 1, "unsupported shape for this kernel");
     __shared__ __attribute__((aligned(16))) bf16 xs[Q * SP];
     __shared__ __attribute__((aligned(16))) bf16 dys[Q * SP];
     __shared__ __attribute__((aligned(16))) bf16 Bs[Q * SN];
@@ -521,10 +530,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Rh[P * SN];
     __shared__ __attribute__((aligned(16))) bf16 Rl[P * SN];
     __shared__ float s2[Q], dtv[Q], ew[Q], es[Q];
-    __shared__ float rowZ[Q], colP[4][Q], offB[Q], offC[Q];
-    __shared__ float red[4];
+    __shared__ float rowP[NH][Q], colP[4][Q], offBP[NH][Q], offCP[NH][Q];
+    __shared__ float red[NW], hrp[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
+    const int band = wave & 3, half = wave >> 2;
+    const int row0 = band * 16;
     const int ci = blockIdx.x / p.G, g = blockIdx.x - ci * p.G;
     if (ci >= p.seq_chunk_start[p.nseq]) return;
     const int4 ce = p.chunks[ci];
@@ -533,137 +544,169 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
     const int o = p.seq_chunk_start[s];
     const int H = p.H, hpg = H / p.G;
     const long long PN = (long long)P * N;
-    const int row0 = wave * 16;
+    const bf16 *xg = reinterpret_cast<const bf16 *>(p.x), *dyg = reinterpret_cast<const bf16 *>(p.dy);
 
-    // rows of a token-major io tensor into a padded LDS tile; all loads first
-    auto stage = [&](auto w_c, bf16 *dst, const bf16 *src, int SW, long long stride, long long col) {
-        constexpr int W = decltype(w_c)::value;
-        constexpr int V8 = W / 8, NV = Q * V8 / 256;
-        bf16x8 v[NV];
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int i = tid + 256 * k, j = i / V8, c8 = (i - j * V8) * 8;
-            v[k] = zero_frag<bf16x8>();
-            if (j < q) v[k] = *reinterpret_cast<const bf16x8 *>(src + (t0 + j) * stride + col + c8);
+    // B and C rows of the chunk (once per group)
+    for (int i = tid; i < Q * (N / 8); i += NTH) {
+        const int j = i / (N / 8), c8 = (i % (N / 8)) * 8;
+        bf16x8 vb = zero_frag<bf16x8>(), vc = zero_frag<bf16x8>();
+        if (j < q) {
+            vb = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const bf16 *>(p.B) + ((t0 + j) * p.G + g) * N + c8);
+            vc = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const bf16 *>(p.C) + ((t0 + j) * p.G + g) * N + c8);
         }
+        *reinterpret_cast<bf16x8 *>(Bs + j * SN + c8) = vb;
+        *reinterpret_cast<bf16x8 *>(Cs + j * SN + c8) = vc;
+    }
+
+    // one head's inputs in registers (loaded a head ahead)
+    bf16x8 xr[XV], dyr[XV];
+    f32x4 hr[SV], rr[SV];
+    float dtr = 0.f;
+    auto load_head = [&](int h) {
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int i = tid + 256 * k, j = i / V8, c8 = (i - j * V8) * 8;
-            *reinterpret_cast<bf16x8 *>(dst + j * SW + c8) = v[k];
+        for (int k = 0; k < XV; ++k) {
+            const int i = tid + NTH * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
+            xr[k] = dyr[k] = zero_frag<bf16x8>();
+            if (i < XP && j < q) {
+                xr[k] = *reinterpret_cast<const bf16x8 *>(xg + ((t0 + j) * H + h) * P + c8);
+                dyr[k] = *reinterpret_cast<const bf16x8 *>(dyg + ((t0 + j) * H + h) * P + c8);
+            }
         }
+        const float *Hc = p.states + ((long long)(o + s + c) * H + h) * PN;
+        const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            const int i = (tid + NTH * k) * 4;
+            hr[k] = rr[k] = zero4();
+            if (i < 4 * SP4) {
+                hr[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
+                rr[k] = *reinterpret_cast<const f32x4 *>(Rc + i);
+            }
+        }
+        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
     };
-    const bf16 *Bg = reinterpret_cast<const bf16 *>(p.B), *Cg = reinterpret_cast<const bf16 *>(p.C);
-    stage(std::integral_constant<int, N>{}, Bs, Bg, SN, (long long)p.G * N, (long long)g * N);
-    stage(std::integral_constant<int, N>{}, Cs, Cg, SN, (long long)p.G * N, (long long)g * N);
 
-    f32x4 dBacc[NT], dCacc[NT];
+    f32x4 dBacc[NT2], dCacc[NT2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) dBacc[nt] = dCacc[nt] = zero4();
+    for (int k = 0; k < NT2; ++k) dBacc[k] = dCacc[k] = zero4();
 
+    if (hpg > 0) load_head(g * hpg);
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
+        // Lane indices re-derived per head: the tiles span more LDS than a ds
+        // offset reaches, and without this the compiler keeps every address
+        // derived from them live across the loop and spills.
+        int tid_ = threadIdx.x;
+        asm volatile("" : "+v"(tid_));
+        const int tid = tid_, lane = tid & 63, li = lane & 15, lg = lane >> 4;
         __syncthreads();   // the previous head's tiles are no longer read
-        const bf16 *xg = reinterpret_cast<const bf16 *>(p.x), *dyg = reinterpret_cast<const bf16 *>(p.dy);
-        stage(std::integral_constant<int, P>{}, xs, xg, SP, (long long)H * P, (long long)h * P);
-        stage(std::integral_constant<int, P>{}, dys, dyg, SP, (long long)H * P, (long long)h * P);
-        const float *Hc = p.states + ((long long)(o + s + c) * H + h) * PN;
-        const float *Hn = p.states + ((long long)(o + s + c + 1) * H + h) * PN;
-        const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
-        float rh = 0.f;
-        // every load of the three state tiles is issued before any is used
-        constexpr int SV = P * N / 1024;   // 4-float pieces per thread
-        f32x4 hvs[SV], rvs[SV], nvs[SV];
+        // this head's registers into LDS
 #pragma unroll
-        for (int k = 0; k < SV; ++k) {
-            const int i = (tid + 256 * k) * 4;
-            hvs[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
-            rvs[k] = *reinterpret_cast<const f32x4 *>(Rc + i);
-            nvs[k] = *reinterpret_cast<const f32x4 *>(Hn + i);
+        for (int k = 0; k < XV; ++k) {
+            const int i = tid + NTH * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
+            if (i < XP) {
+                *reinterpret_cast<bf16x8 *>(xs + j * SP + c8) = xr[k];
+                *reinterpret_cast<bf16x8 *>(dys + j * SP + c8) = dyr[k];
+            }
         }
+        float hrd = 0.f;   // <R_c, H_c>
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
-            const int i = (tid + 256 * k) * 4;
-            const f32x4 hv = hvs[k], rv = rvs[k], nv = nvs[k];
+            const int i = (tid + NTH * k) * 4;
+            if (i >= 4 * SP4) break;
             const int pp = i / N, nn = i - pp * N;
             bf16x4 a, b, cc, d;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                a[e] = (bf16)hv[e];
-                b[e] = (bf16)(hv[e] - (float)a[e]);
-                cc[e] = (bf16)rv[e];
-                d[e] = (bf16)(rv[e] - (float)cc[e]);
-                rh += rv[e] * nv[e];
+                hrd += hr[k][e] * rr[k][e];
+                a[e] = (bf16)hr[k][e];
+                b[e] = (bf16)(hr[k][e] - (float)a[e]);
+                cc[e] = (bf16)rr[k][e];
+                d[e] = (bf16)(rr[k][e] - (float)cc[e]);
             }
             *reinterpret_cast<bf16x4 *>(Hh + pp * SN + nn) = a;
             *reinterpret_cast<bf16x4 *>(Hl + pp * SN + nn) = b;
             *reinterpret_cast<bf16x4 *>(Rh + pp * SN + nn) = cc;
             *reinterpret_cast<bf16x4 *>(Rl + pp * SN + nn) = d;
         }
+        hrd = bwd_wave_sum(hrd);
+        if (lane == 0) hrp[wave] = hrd;
         const float Ah = p.A[h];
         if (wave == 0) {
-            const float d = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
-            const float sc = bwd_wave_scan(d * Ah, lane) * kBwdLog2e;
+            const float sc = bwd_wave_scan(dtr * Ah, lane) * kBwdLog2e;
             const float slast = __shfl(sc, 63, 64);
             s2[lane] = sc;
-            dtv[lane] = d;
+            dtv[lane] = dtr;
             ew[lane] = __builtin_amdgcn_exp2f(slast - sc);
             es[lane] = __builtin_amdgcn_exp2f(sc);
         }
-        rh = block_sum(rh, red);   // (its barriers also publish the tiles above)
+        __syncthreads();
+        if (hh + 1 < hpg) load_head(h + 1);   // in flight during this head's MFMAs
 
-        // C B^T and dY X^T for rows row0..row0+15, then M, W and the Z sums
+        // C B^T and dY X^T for rows row0..row0+15, this part's columns; M, W and the Z sums
         {
-            f32x4 gt[4], et[4];
+            constexpr int JT = 4 / NH;   // 16-column tiles of the chunk per part
+            f32x4 gt[JT], et[JT];
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                gt[jt] = et[jt] = zero4();
+            for (int u = 0; u < JT; ++u) {
+                const int jt = JT * half + u;
+                gt[u] = et[u] = zero4();
 #pragma unroll
                 for (int k0 = 0; k0 < N; k0 += 32)
-                    gt[jt] = mfma_bf16(gt[jt], frag_row<SN>(Cs, row0 + li, k0, lg), frag_row<SN>(Bs, jt * 16 + li, k0, lg));
+                    gt[u] = mfma_bf16(gt[u], frag_row<SN>(Cs, row0 + li, k0, lg), frag_row<SN>(Bs, jt * 16 + li, k0, lg));
 #pragma unroll
                 for (int k0 = 0; k0 < P; k0 += 32)
-                    et[jt] = mfma_bf16(et[jt], frag_row<SP>(dys, row0 + li, k0, lg), frag_row<SP>(xs, jt * 16 + li, k0, lg));
+                    et[u] = mfma_bf16(et[u], frag_row<SP>(dys, row0 + li, k0, lg), frag_row<SP>(xs, jt * 16 + li, k0, lg));
             }
             float rz[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const int j = jt * 16 + li;
+            for (int u = 0; u < JT; ++u) {
+                const int j = (JT * half + u) * 16 + li;
                 const float sj = s2[j], dj = dtv[j];
                 float cz = 0.f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = row0 + 4 * lg + r;
                     const float dec = j <= i ? __builtin_amdgcn_exp2f(s2[i] - sj) : 0.f;
-                    const float z = gt[jt][r] * et[jt][r] * dec;
+                    const float z = gt[u][r] * et[u][r] * dec;
                     rz[r] += z * dj;
                     cz += z;
-                    Ms[i * SQ + j] = (bf16)(gt[jt][r] * dec * dj);
-                    Ws[i * SQ + j] = (bf16)(et[jt][r] * dec * dj);
+                    Ms[i * SQ + j] = (bf16)(gt[u][r] * dec * dj);
+                    Ws[i * SQ + j] = (bf16)(et[u][r] * dec * dj);
                 }
                 cz += __shfl_xor(cz, 16, 64);
                 cz += __shfl_xor(cz, 32, 64);
-                if (lg == 0) colP[wave][j] = cz;
+                if (lg == 0) colP[band][j] = cz;
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
 #pragma unroll
                 for (int m = 1; m < 16; m <<= 1) rz[r] += __shfl_xor(rz[r], m, 64);
-                if (li == 0) rowZ[row0 + 4 * lg + r] = rz[r];
+                if (li == 0) rowP[half][row0 + 4 * lg + r] = rz[r];
             }
         }
-        float dd = 0.f;   // dy . x over the chunk
-        for (int i = tid; i < Q * P; i += 256) {
+        // dy . x over the chunk (one element per thread and piece)
+        float dd = 0.f;
+        for (int i = tid; i < Q * P; i += NTH) {
             const int j = i / P, pp = i - j * P;
             dd += (float)dys[j * SP + pp] * (float)xs[j * SP + pp];
         }
-        dd = block_sum(dd, red);   // (also publishes M and W)
-        if (tid == 0) p.partD[(long long)ci * H + h] = dd;
+        dd = bwd_wave_sum(dd);
+        if (lane == 0) red[wave] = dd;
+        __syncthreads();   // M, W, partial sums
+        if (tid == 0) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += red[w];
+            p.partD[(long long)ci * H + h] = t;
+        }
 
-        // dx = M^T dY + diag(w) B R^T + D dY
+        // dx = M^T dY + diag(w) B R^T + D dY (this band, this half's columns)
         const float Dh = p.D ? p.D[h] : 0.f;
         bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
+        for (int u = 0; u < PT2; ++u) {
+            const int pt = half * PT2 + u;
             f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < Q; k0 += 32)
@@ -680,34 +723,34 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
             }
         }
 
-        // dB, dC of this head and the row dot products of their low-rank parts
+        // dB, dC of this head (this half's columns) and the row dot products
         float ob[4] = {0.f, 0.f, 0.f, 0.f}, oc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int u = 0; u < NT2; ++u) {
+            const int nt = half * NT2 + u;
             f32x4 db = zero4(), dc = zero4(), xb = zero4(), yc = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < Q; k0 += 32) {
                 db = mfma_bf16(db, frag_col<SQ>(Ws, k0, row0, li, lg), frag_col<SN>(Cs, k0, nt * 16, li, lg));
-                const bf16x8 bcol = frag_col<SN>(Bs, k0, nt * 16, li, lg);
-                dc = mfma_bf16(dc, frag_row<SQ>(Ws, row0 + li, k0, lg), bcol);
+                dc = mfma_bf16(dc, frag_row<SQ>(Ws, row0 + li, k0, lg), frag_col<SN>(Bs, k0, nt * 16, li, lg));
             }
 #pragma unroll
             for (int k0 = 0; k0 < P; k0 += 32) {
-                const bf16x8 xr = frag_row<SP>(xs, row0 + li, k0, lg);
-                xb = mfma_bf16(xb, xr, frag_col<SN>(Rh, k0, nt * 16, li, lg));
-                xb = mfma_bf16(xb, xr, frag_col<SN>(Rl, k0, nt * 16, li, lg));
-                const bf16x8 yr = frag_row<SP>(dys, row0 + li, k0, lg);
-                yc = mfma_bf16(yc, yr, frag_col<SN>(Hh, k0, nt * 16, li, lg));
-                yc = mfma_bf16(yc, yr, frag_col<SN>(Hl, k0, nt * 16, li, lg));
+                const bf16x8 xrow = frag_row<SP>(xs, row0 + li, k0, lg);
+                xb = mfma_bf16(xb, xrow, frag_col<SN>(Rh, k0, nt * 16, li, lg));
+                xb = mfma_bf16(xb, xrow, frag_col<SN>(Rl, k0, nt * 16, li, lg));
+                const bf16x8 yrow = frag_row<SP>(dys, row0 + li, k0, lg);
+                yc = mfma_bf16(yc, yrow, frag_col<SN>(Hh, k0, nt * 16, li, lg));
+                yc = mfma_bf16(yc, yrow, frag_col<SN>(Hl, k0, nt * 16, li, lg));
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int rr = row0 + 4 * lg + r, nn = nt * 16 + li;
-                const float xbr = xb[r] * ew[rr], ycr = yc[r] * es[rr];
-                dBacc[nt][r] += db[r] + dtv[rr] * xbr;
-                dCacc[nt][r] += dc[r] + ycr;
-                ob[r] += xbr * (float)Bs[rr * SN + nn];
-                oc[r] += ycr * (float)Cs[rr * SN + nn];
+                const int rw = row0 + 4 * lg + r, nn = nt * 16 + li;
+                const float xbr = xb[r] * ew[rw], ycr = yc[r] * es[rw];
+                dBacc[u][r] += db[r] + dtv[rw] * xbr;
+                dCacc[u][r] += dc[r] + ycr;
+                ob[r] += xbr * (float)Bs[rw * SN + nn];
+                oc[r] += ycr * (float)Cs[rw * SN + nn];
             }
         }
 #pragma unroll
@@ -718,8 +761,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
                 oc[r] += __shfl_xor(oc[r], m, 64);
             }
             if (li == 0) {
-                offB[row0 + 4 * lg + r] = ob[r];
-                offC[row0 + 4 * lg + r] = oc[r];
+                offBP[half][row0 + 4 * lg + r] = ob[r];
+                offCP[half][row0 + 4 * lg + r] = oc[r];
             }
         }
         __syncthreads();
@@ -728,23 +771,35 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_bf16_kernel(BwdParams p) {
             const int j = lane;
             const float d = dtv[j];
             const float cz = colP[0][j] + colP[1][j] + colP[2][j] + colP[3][j];
-            const float ds = rowZ[j] - d * cz + offC[j] - d * offB[j] + (j == q - 1 ? rh : 0.f);
+            float ob_ = 0.f, rz = 0.f, oc_ = 0.f;
+#pragma unroll
+            for (int u = 0; u < NH; ++u) {
+                ob_ += offBP[u][j];
+                rz += rowP[u][j];
+                oc_ += offCP[u][j];
+            }
+            float hrs = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) hrs += hrp[w];
+            // <R_c, H_{c+1}> = exp(s_last) <R_c, H_c> + <R_c, S_c>, and <R_c, S_c> = sum_j dt_j offB_j
+            const float rh = __builtin_amdgcn_exp2f(s2[Q - 1]) * hrs + bwd_wave_sum(d * ob_);
+            const float ds = rz - d * cz + oc_ - d * ob_ + (j == q - 1 ? rh : 0.f);
             const float tot = bwd_wave_sum(ds);
             const float da = tot - bwd_wave_scan(ds, lane) + ds;
-            if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + cz + offB[j];
+            if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + cz + ob_;
             const float pa = bwd_wave_sum(d * da);
             if (lane == 0) p.partA[(long long)ci * H + h] = pa;
         }
     }
 
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int u = 0; u < NT2; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int rr = row0 + 4 * lg + r, nn = nt * 16 + li;
-            if (rr < q) {
-                p.dB[((t0 + rr) * p.G + g) * N + nn] = dBacc[nt][r];
-                p.dC[((t0 + rr) * p.G + g) * N + nn] = dCacc[nt][r];
+            const int rw = row0 + 4 * lg + r, nn = (half * NT2 + u) * 16 + li;
+            if (rw < q) {
+                p.dB[((t0 + rw) * p.G + g) * N + nn] = dBacc[u][r];
+                p.dC[((t0 + rw) * p.G + g) * N + nn] = dCacc[u][r];
             }
         }
 }
