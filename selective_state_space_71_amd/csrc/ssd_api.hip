@@ -291,8 +291,7 @@ static bool bwd_try(int pp, int nn, const BwdParams &p, unsigned units, unsigned
     if (pp != P || nn != N) return false;
     if (launch) {
         if constexpr (sizeof(IO) == 2 && P >= 32 && N >= 32) {
-            hipLaunchKernelGGL((ssd_bwd_scan_bf16_kernel<P, N, 0>), dim3(units), dim3(256), 0, st, p);
-            hipLaunchKernelGGL((ssd_bwd_scan_bf16_kernel<P, N, 1>), dim3(units), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((ssd_bwd_scan_bf16_kernel<P, N>), dim3(2 * units), dim3(256), 0, st, p);
         } else {
             hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 0>), dim3(units), dim3(256), 0, st, p);
             hipLaunchKernelGGL((ssd_bwd_scan_kernel<IO, P, N, 1>), dim3(units), dim3(256), 0, st, p);

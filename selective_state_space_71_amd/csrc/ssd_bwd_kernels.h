@@ -804,13 +804,15 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
 }
 
-// bf16 version of the chunk-sequential scan for headdim and dstate >= 32.  The
-// next chunk's rows and dt are loaded into registers while the current chunk
-// is computed; u is scaled by the decay weights once per chunk and kept in LDS
+// bf16 version of the chunk-sequential scans for headdim and dstate >= 32.
+// The two scans are independent, so one launch runs both (twice the
+// workgroups of either: the chains are latency-bound), and its register
+// budget allows three workgroups per compute unit.  The next chunk's rows
+// and dt are loaded into registers while the current chunk is computed; u is scaled by the decay weights once per chunk and kept in LDS
 // as a split bf16 pair, and both MFMA operands are read in the K-slot order
 // with transposing LDS reads.
-template <int P, int N, int MODE>
-__global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
+template <int P, int N>
+__global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
     constexpr int Q = kBwdQ;
     constexpr int PT = P / 16, NT = N / 16, TILES = PT * NT;
     constexpr int TPW = (TILES + 3) / 4;
@@ -825,17 +827,21 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
     __shared__ float salpha;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int s = blockIdx.x / p.H, h = blockIdx.x - s * p.H;
+    // blocks [0, nseq H): forward boundary states (mode 0); [nseq H, 2 nseq H): the reverse chain (mode 1)
+    const int units = p.nseq * p.H;
+    const int mode = blockIdx.x >= units;
+    const int unit = blockIdx.x - mode * units;
+    const int s = unit / p.H, h = unit - s * p.H;
     const int g = h / (p.H / p.G);
     const int o = p.seq_chunk_start[s];
     const int nc = p.seq_chunk_start[s + 1] - o;
     const long long PN = (long long)P * N;
-    const bf16 *ug = reinterpret_cast<const bf16 *>(MODE == 0 ? p.x : p.dy);
-    const bf16 *vg = reinterpret_cast<const bf16 *>(MODE == 0 ? p.B : p.C);
+    const bf16 *ug = reinterpret_cast<const bf16 *>(mode == 0 ? p.x : p.dy);
+    const bf16 *vg = reinterpret_cast<const bf16 *>(mode == 0 ? p.B : p.C);
     const float Ah = p.A[h];
 
     f32x4 st[TPW];
-    const float *st0 = MODE == 0 ? p.init_state : p.dfinal;
+    const float *st0 = mode == 0 ? p.init_state : p.dfinal;
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
         const int t = wave + 4 * k;
@@ -855,7 +861,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
             }
         }
     };
-    if (MODE == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
+    if (mode == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
 
     // registers of one chunk: u and v pieces (row j, 8 columns) and dt (wave 0)
     bf16x8 ur[UV], vr[VV];
@@ -878,10 +884,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
         }
         if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * p.H + h] : 0.f;
     };
-    if (nc > 0) load_chunk(MODE == 0 ? 0 : nc - 1);
+    if (nc > 0) load_chunk(mode == 0 ? 0 : nc - 1);
 
     for (int step = 0; step < nc; ++step) {
-        const int c = MODE == 0 ? step : nc - 1 - step;
+        const int c = mode == 0 ? step : nc - 1 - step;
         // v rows and the weights of this chunk into LDS
 #pragma unroll
         for (int k = 0; k < VV; ++k) {
@@ -891,7 +897,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
         if (wave == 0) {
             const float sc = bwd_wave_scan(dtr * Ah, lane) * kBwdLog2e;
             const float slast = __shfl(sc, 63, 64);
-            swt[lane] = MODE == 0 ? __builtin_amdgcn_exp2f(slast - sc) * dtr : __builtin_amdgcn_exp2f(sc);
+            swt[lane] = mode == 0 ? __builtin_amdgcn_exp2f(slast - sc) * dtr : __builtin_amdgcn_exp2f(sc);
             if (lane == 0) salpha = __builtin_amdgcn_exp2f(slast);
         }
         __syncthreads();
@@ -912,8 +918,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
         }
         const float alpha = salpha;
         __syncthreads();
-        if (step + 1 < nc) load_chunk(MODE == 0 ? c + 1 : c - 1);   // in flight during the MFMAs
-        if (MODE == 1) store_state(p.radj + ((long long)(o + c) * p.H + h) * PN);
+        if (step + 1 < nc) load_chunk(mode == 0 ? c + 1 : c - 1);   // in flight during the MFMAs
+        if (mode == 1) store_state(p.radj + ((long long)(o + c) * p.H + h) * PN);
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
             const int t = wave + 4 * k;
@@ -931,10 +937,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
                 for (int r = 0; r < 4; ++r) st[k][r] = alpha * st[k][r] + acc[r];
             }
         }
-        if (MODE == 0) store_state(p.states + ((long long)(o + s + c + 1) * p.H + h) * PN);
+        if (mode == 0) store_state(p.states + ((long long)(o + s + c + 1) * p.H + h) * PN);
         __syncthreads();   // the LDS tiles are rewritten by the next chunk
     }
-    if (MODE == 1 && p.dinit) store_state(p.dinit + ((long long)s * p.H + h) * PN);
+    if (mode == 1 && p.dinit) store_state(p.dinit + ((long long)s * p.H + h) * PN);
 }
 
 // dA[h], dD[h]: sums of the per-chunk partials, one workgroup per head, in a
