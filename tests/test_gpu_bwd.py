@@ -50,6 +50,10 @@ def _ref(inp, unit_mask=None):
     ("bf16", 1, 130, 4, 32, 64, 2, None),
     ("bf16", 1, 200, 2, 64, 128, 1, [64, 0, 1, 100, 35]),
     ("bf16", 1, 64, 2, 16, 16, 1, None),
+    ("bf16", 1, 150, 2, 64, 32, 1, None),
+    ("bf16", 1, 100, 3, 32, 32, 1, [30, 70]),
+    ("bf16", 1, 90, 2, 32, 128, 1, None),
+    ("bf16", 2, 77, 2, 64, 64, 2, None),
     ("f32", 1, 100, 2, 16, 16, 1, None),
     ("f32", 2, 70, 2, 64, 64, 1, None),
     ("f32", 1, 90, 4, 32, 32, 2, [30, 60]),
