@@ -80,19 +80,39 @@ __device__ __forceinline__ f32x4 mma_tile(f32x4 acc, int K, int lg, FA fa, FB fb
 template <typename IO> __device__ __forceinline__ float split_hi(float v) { return to_f32(from_f32<IO>(v)); }
 template <typename IO> __device__ __forceinline__ float split_lo(float v) { return v - split_hi<IO>(v); }
 
-__device__ __forceinline__ float bwd_wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// v + (v of the lane the DPP control `ctrl` selects); lanes without a source
+// (or outside `row_mask`) add 0.
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float bwd_dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask, 0xF, true);
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Sum over the 16 lanes of each row of the wave, in every lane of the row:
+// pairs, quads, then the mirrored half and the mirrored row.
+__device__ __forceinline__ float bwd_row_sum(float v) {
+    v = bwd_dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = bwd_dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = bwd_dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = bwd_dpp_add<0x140, 0xF>(v);   // row_mirror
     return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (log-step shuffles).
-__device__ __forceinline__ float bwd_wave_scan(float v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
+// Sum over the 64 lanes (wave-uniform result), in a fixed order.
+__device__ __forceinline__ float bwd_wave_sum(float v) {
+    v = bwd_row_sum(v);
+    const auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+    return (rl(0) + rl(16)) + (rl(32) + rl(48));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float bwd_wave_scan(float v, int) {
+    v = bwd_dpp_add<0x111, 0xF>(v);   // row_shr:1
+    v = bwd_dpp_add<0x112, 0xF>(v);   // row_shr:2
+    v = bwd_dpp_add<0x114, 0xF>(v);   // row_shr:4
+    v = bwd_dpp_add<0x118, 0xF>(v);   // row_shr:8
+    v = bwd_dpp_add<0x142, 0xA>(v);   // row_bcast:15
+    v = bwd_dpp_add<0x143, 0xC>(v);   // row_bcast:31
     return v;
 }
 
@@ -558,11 +578,21 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         *reinterpret_cast<bf16x8 *>(Cs + j * SN + c8) = vc;
     }
 
-    // one head's inputs in registers (loaded a head ahead)
+    // one head's inputs in registers (loaded a head ahead; R issued later than
+    // the rest, so that the loads do not all queue behind one barrier)
     bf16x8 xr[XV], dyr[XV];
     f32x4 hr[SV], rr[SV];
     float dtr = 0.f;
-    auto load_head = [&](int h) {
+    auto load_r = [&](int h) {
+        const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            const int i = (tid + NTH * k) * 4;
+            rr[k] = zero4();
+            if (i < 4 * SP4) rr[k] = *reinterpret_cast<const f32x4 *>(Rc + i);
+        }
+    };
+    auto load_head = [&](int h, bool with_r) {
 #pragma unroll
         for (int k = 0; k < XV; ++k) {
             const int i = tid + NTH * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
@@ -577,20 +607,18 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             const int i = (tid + NTH * k) * 4;
-            hr[k] = rr[k] = zero4();
-            if (i < 4 * SP4) {
-                hr[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
-                rr[k] = *reinterpret_cast<const f32x4 *>(Rc + i);
-            }
+            hr[k] = zero4();
+            if (i < 4 * SP4) hr[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
         }
         if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
+        if (with_r) load_r(h);
     };
 
     f32x4 dBacc[NT2], dCacc[NT2];
 #pragma unroll
     for (int k = 0; k < NT2; ++k) dBacc[k] = dCacc[k] = zero4();
 
-    if (hpg > 0) load_head(g * hpg);
+    if (hpg > 0) load_head(g * hpg, true);
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         // Lane indices re-derived per head: the tiles span more LDS than a ds
@@ -600,13 +628,16 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         asm volatile("" : "+v"(tid_));
         const int tid = tid_, lane = tid & 63, li = lane & 15, lg = lane >> 4;
         __syncthreads();   // the previous head's tiles are no longer read
-        // this head's registers into LDS
+        // this head's registers into LDS; dy . x over the chunk from the same registers
+        float dd = 0.f;
 #pragma unroll
         for (int k = 0; k < XV; ++k) {
             const int i = tid + NTH * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
             if (i < XP) {
                 *reinterpret_cast<bf16x8 *>(xs + j * SP + c8) = xr[k];
                 *reinterpret_cast<bf16x8 *>(dys + j * SP + c8) = dyr[k];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dd += (float)xr[k][e] * (float)dyr[k][e];
             }
         }
         float hrd = 0.f;   // <R_c, H_c>
@@ -641,7 +672,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             es[lane] = __builtin_amdgcn_exp2f(sc);
         }
         __syncthreads();
-        if (hh + 1 < hpg) load_head(h + 1);   // in flight during this head's MFMAs
+        if (hh + 1 < hpg) load_head(h + 1, false);   // in flight during this head's MFMAs
 
         // C B^T and dY X^T for rows row0..row0+15, this part's columns; M, W and the Z sums
         {
@@ -680,16 +711,9 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) rz[r] += __shfl_xor(rz[r], m, 64);
+                rz[r] = bwd_row_sum(rz[r]);
                 if (li == 0) rowP[half][row0 + 4 * lg + r] = rz[r];
             }
-        }
-        // dy . x over the chunk (one element per thread and piece)
-        float dd = 0.f;
-        for (int i = tid; i < Q * P; i += NTH) {
-            const int j = i / P, pp = i - j * P;
-            dd += (float)dys[j * SP + pp] * (float)xs[j * SP + pp];
         }
         dd = bwd_wave_sum(dd);
         if (lane == 0) red[wave] = dd;
@@ -701,6 +725,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             p.partD[(long long)ci * H + h] = t;
         }
 
+        if (hh + 1 < hpg) load_r(h + 1);
         // dx = M^T dY + diag(w) B R^T + D dY (this band, this half's columns)
         const float Dh = p.D ? p.D[h] : 0.f;
         bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
@@ -755,11 +780,8 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-                ob[r] += __shfl_xor(ob[r], m, 64);
-                oc[r] += __shfl_xor(oc[r], m, 64);
-            }
+            ob[r] = bwd_row_sum(ob[r]);
+            oc[r] = bwd_row_sum(oc[r]);
             if (li == 0) {
                 offBP[half][row0 + 4 * lg + r] = ob[r];
                 offCP[half][row0 + 4 * lg + r] = oc[r];
