@@ -501,10 +501,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
 // operand is read from LDS in the K-slot order of the forward kernel (slot e
 // of lane group lg holds k0 + 16 (e / 4) + 4 lg + e % 4): two 8-byte reads for
 // an operand whose K index runs along its rows, or two transposing reads when
-// it runs down its columns.  Per head, C B^T and dY X^T are formed in
-// registers (a 16-row band per wave); the decayed, masked M and W go to LDS
-// once, and the row/column sums of their product come from the same
-// registers.  H and R are kept as split bf16 pairs.
+// it runs down its columns.  C B^T is formed in registers once per chunk; per
+// head, dY X^T is formed in registers (a 16-row band per wave), the decayed,
+// masked M goes to LDS, W is summed over the heads in registers, and the
+// row/column sums of their product come from the same registers.  H and R are
+// kept as split bf16 pairs.
 template <int S>
 __device__ __forceinline__ bf16x8 frag_row(const bf16 *base, int m, int k0, int lg) {
     const bf16 *q = base + m * S + k0 + 4 * lg;
@@ -576,6 +577,22 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
         *reinterpret_cast<bf16x8 *>(Bs + j * SN + c8) = vb;
         *reinterpret_cast<bf16x8 *>(Cs + j * SN + c8) = vc;
+    }
+    __syncthreads();   // B and C rows in LDS
+
+    // C B^T does not depend on the head: this wave's tiles (row band `band`,
+    // column tiles JT half ..) are formed once.  W is only ever multiplied by
+    // the head-independent B and C, so sum_h W_h is accumulated here and its
+    // products with C and B are formed once, after the head loop.
+    constexpr int JT = 4 / NH;   // 16-column tiles of the chunk per part
+    f32x4 gt[JT], wacc[JT];
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int jt = JT * half + u;
+        gt[u] = wacc[u] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < N; k0 += 32)
+            gt[u] = mfma_bf16(gt[u], frag_row<SN>(Cs, row0 + li, k0, lg), frag_row<SN>(Bs, jt * 16 + li, k0, lg));
     }
 
     // one head's inputs in registers (loaded a head ahead; R issued later than
@@ -674,17 +691,13 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         __syncthreads();
         if (hh + 1 < hpg) load_head(h + 1, false);   // in flight during this head's MFMAs
 
-        // C B^T and dY X^T for rows row0..row0+15, this part's columns; M, W and the Z sums
+        // dY X^T for rows row0..row0+15, this part's columns; M, the W sum and the Z sums
         {
-            constexpr int JT = 4 / NH;   // 16-column tiles of the chunk per part
-            f32x4 gt[JT], et[JT];
+            f32x4 et[JT];
 #pragma unroll
             for (int u = 0; u < JT; ++u) {
                 const int jt = JT * half + u;
-                gt[u] = et[u] = zero4();
-#pragma unroll
-                for (int k0 = 0; k0 < N; k0 += 32)
-                    gt[u] = mfma_bf16(gt[u], frag_row<SN>(Cs, row0 + li, k0, lg), frag_row<SN>(Bs, jt * 16 + li, k0, lg));
+                et[u] = zero4();
 #pragma unroll
                 for (int k0 = 0; k0 < P; k0 += 32)
                     et[u] = mfma_bf16(et[u], frag_row<SP>(dys, row0 + li, k0, lg), frag_row<SP>(xs, jt * 16 + li, k0, lg));
@@ -703,7 +716,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
                     rz[r] += z * dj;
                     cz += z;
                     Ms[i * SQ + j] = (bf16)(gt[u][r] * dec * dj);
-                    Ws[i * SQ + j] = (bf16)(et[u][r] * dec * dj);
+                    wacc[u][r] += et[u][r] * dec * dj;
                 }
                 cz += __shfl_xor(cz, 16, 64);
                 cz += __shfl_xor(cz, 32, 64);
@@ -717,7 +730,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
         dd = bwd_wave_sum(dd);
         if (lane == 0) red[wave] = dd;
-        __syncthreads();   // M, W, partial sums
+        __syncthreads();   // M, partial sums
         if (tid == 0) {
             float t = 0.f;
 #pragma unroll
@@ -753,12 +766,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
 #pragma unroll
         for (int u = 0; u < NT2; ++u) {
             const int nt = half * NT2 + u;
-            f32x4 db = zero4(), dc = zero4(), xb = zero4(), yc = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < Q; k0 += 32) {
-                db = mfma_bf16(db, frag_col<SQ>(Ws, k0, row0, li, lg), frag_col<SN>(Cs, k0, nt * 16, li, lg));
-                dc = mfma_bf16(dc, frag_row<SQ>(Ws, row0 + li, k0, lg), frag_col<SN>(Bs, k0, nt * 16, li, lg));
-            }
+            f32x4 xb = zero4(), yc = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < P; k0 += 32) {
                 const bf16x8 xrow = frag_row<SP>(xs, row0 + li, k0, lg);
@@ -772,8 +780,8 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             for (int r = 0; r < 4; ++r) {
                 const int rw = row0 + 4 * lg + r, nn = nt * 16 + li;
                 const float xbr = xb[r] * ew[rw], ycr = yc[r] * es[rw];
-                dBacc[u][r] += db[r] + dtv[rw] * xbr;
-                dCacc[u][r] += dc[r] + ycr;
+                dBacc[u][r] += dtv[rw] * xbr;
+                dCacc[u][r] += ycr;
                 ob[r] += xbr * (float)Bs[rw * SN + nn];
                 oc[r] += ycr * (float)Cs[rw * SN + nn];
             }
@@ -814,6 +822,39 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
     }
 
+    // diagonal parts of dB and dC: (sum_h W_h)^T C and (sum_h W_h) B, with the
+    // sum as a split bf16 pair (high parts in Ms, remainders in Ws)
+    __syncthreads();   // every wave is done with the last head's tiles
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int j = (JT * half + u) * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * lg + r;
+            const bf16 hi = (bf16)wacc[u][r];
+            Ms[i * SQ + j] = hi;
+            Ws[i * SQ + j] = (bf16)(wacc[u][r] - (float)hi);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NT2; ++u) {
+        const int nt = half * NT2 + u;
+        f32x4 db = zero4(), dc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < Q; k0 += 32) {
+            const bf16x8 cf = frag_col<SN>(Cs, k0, nt * 16, li, lg), bfr = frag_col<SN>(Bs, k0, nt * 16, li, lg);
+            db = mfma_bf16(db, frag_col<SQ>(Ms, k0, row0, li, lg), cf);
+            db = mfma_bf16(db, frag_col<SQ>(Ws, k0, row0, li, lg), cf);
+            dc = mfma_bf16(dc, frag_row<SQ>(Ms, row0 + li, k0, lg), bfr);
+            dc = mfma_bf16(dc, frag_row<SQ>(Ws, row0 + li, k0, lg), bfr);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dBacc[u][r] += db[r];
+            dCacc[u][r] += dc[r];
+        }
+    }
 #pragma unroll
     for (int u = 0; u < NT2; ++u)
 #pragma unroll
