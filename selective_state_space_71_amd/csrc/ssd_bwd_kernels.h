@@ -742,22 +742,27 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         // dx = M^T dY + diag(w) B R^T + D dY (this band, this half's columns)
         const float Dh = p.D ? p.D[h] : 0.f;
         bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
+        // computed transposed (rows head-dim, columns tokens), so that each lane
+        // holds 4 consecutive head-dim entries of one token: one 8-byte dy read
+        // and one 8-byte store per tile
 #pragma unroll
         for (int u = 0; u < PT2; ++u) {
             const int pt = half * PT2 + u;
             f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < Q; k0 += 32)
-                a1 = mfma_bf16(a1, frag_col<SQ>(Ms, k0, row0, li, lg), frag_col<SP>(dys, k0, pt * 16, li, lg));
+                a1 = mfma_bf16(a1, frag_col<SP>(dys, k0, pt * 16, li, lg), frag_col<SQ>(Ms, k0, row0, li, lg));
 #pragma unroll
             for (int k0 = 0; k0 < N; k0 += 32)
-                a2 = mfma_bf16(a2, frag_row<SN>(Bs, row0 + li, k0, lg), frag_row<SN>(Rh, pt * 16 + li, k0, lg));
+                a2 = mfma_bf16(a2, frag_row<SN>(Rh, pt * 16 + li, k0, lg), frag_row<SN>(Bs, row0 + li, k0, lg));
+            const int j = row0 + li, p0 = pt * 16 + 4 * lg;
+            if (j < q) {
+                const float wj = ew[j] * dtv[j];
+                const bf16x4 dyv = *reinterpret_cast<const bf16x4 *>(dys + j * SP + p0);
+                bf16x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = row0 + 4 * lg + r, pp = pt * 16 + li;
-                if (j < q)
-                    dxg[((t0 + j) * H + h) * P + pp] =
-                        (bf16)(a1[r] + ew[j] * dtv[j] * a2[r] + Dh * (float)dys[j * SP + pp]);
+                for (int r = 0; r < 4; ++r) o[r] = (bf16)(a1[r] + wj * a2[r] + Dh * (float)dyv[r]);
+                *reinterpret_cast<bf16x4 *>(dxg + ((t0 + j) * H + h) * P + p0) = o;
             }
         }
 
