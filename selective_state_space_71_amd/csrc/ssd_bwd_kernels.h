@@ -620,7 +620,6 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             }
         }
         const float *Hc = p.states + ((long long)(o + s + c) * H + h) * PN;
-        const float *Rc = p.radj + ((long long)(o + c) * H + h) * PN;
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             const int i = (tid + NTH * k) * 4;
@@ -897,8 +896,8 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
     const int li = lane & 15, lg = lane >> 4;
     // blocks [0, nseq H): forward boundary states (mode 0); [nseq H, 2 nseq H): the reverse chain (mode 1)
     const int units = p.nseq * p.H;
-    const int mode = blockIdx.x >= units;
-    const int unit = blockIdx.x - mode * units;
+    const int mode = (int)blockIdx.x >= units;
+    const int unit = (int)blockIdx.x - mode * units;
     const int s = unit / p.H, h = unit - s * p.H;
     const int g = h / (p.H / p.G);
     const int o = p.seq_chunk_start[s];

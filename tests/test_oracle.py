@@ -512,3 +512,37 @@ def test_backward_euler_identities():
     assert abs(np.sum(g0["dC"] * p["C"]) - np.sum(dy * y0)) < 1e-9 * abs(L0) + 1e-9
     # dD is the plain contraction of dy with x
     np.testing.assert_allclose(g["dD"], np.einsum("blhp,blhp->h", dy, p["x"]), rtol=1e-12)
+
+
+def test_last_token_state_term_identity():
+    """The GPU backward forms <R, H_{c+1}> (the state term of dL/ds at a chunk's
+    last token) as exp(s_last) <R, H_c> + sum_j dt_j exp(s_last - s_j) (X R)_j . B_j,
+    i.e. H_{c+1} expanded by one chunk of the recurrence (Review 3-2(4): the
+    chunk state S_c and the boundary-state update).  Pinned on the oracle's
+    own states: H_c and H_{c+1} from prefix runs of the fp64 recurrence, R
+    arbitrary."""
+    rng = np.random.default_rng(11)
+    H, P, N, G = 3, 4, 5, 1
+    L0, q = 9, 7                         # the chunk is tokens [L0, L0 + q)
+    L = L0 + q
+    x = rng.standard_normal((1, L, H, P))
+    dt = rng.uniform(0.01, 0.3, (1, L, H))
+    A = -rng.uniform(0.5, 2.0, H)
+    B = rng.standard_normal((1, L, G, N))
+    C = rng.standard_normal((1, L, G, N))
+    h0 = rng.standard_normal((1, H, P, N))
+    _, Hc = oracle.ssd_fwd(x[:, :L0], dt[:, :L0], A, B[:, :L0], C[:, :L0], init_state=h0)
+    _, Hn = oracle.ssd_fwd(x, dt, A, B, C, init_state=h0)
+    R = rng.standard_normal((H, P, N))
+    for h in range(H):
+        s = np.cumsum(dt[0, L0:, h] * A[h])
+        w = dt[0, L0:, h] * np.exp(s[-1] - s)
+        X, Bc = x[0, L0:, h], B[0, L0:, 0]
+        lhs = np.sum(R[h] * Hn[0, h])
+        rhs = np.exp(s[-1]) * np.sum(R[h] * Hc[0, h]) + np.sum(w * np.einsum("jp,pn,jn->j", X, R[h], Bc))
+        assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + 1.0), (h, lhs, rhs)
+    # a wrong decay (exp(s_last) dropped) must break it
+    s = np.cumsum(dt[0, L0:, 0] * A[0])
+    bad = np.sum(R[0] * Hc[0, 0]) + np.sum(dt[0, L0:, 0] * np.exp(s[-1] - s) *
+                                          np.einsum("jp,pn,jn->j", x[0, L0:, 0], R[0], B[0, L0:, 0]))
+    assert abs(np.sum(R[0] * Hn[0, 0]) - bad) > 1e-6
