@@ -96,3 +96,30 @@ def test_backward_full_size_sampled_heads():
     print("[bwd full] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
         assert v <= 1e-2, (k, v)
+
+
+def test_backward_varlen_grouped_full_size_sampled_heads():
+    """The packed variable-length workload (16 sequences, 65,536 tokens, 32
+    heads in 8 groups, no initial state): every gradient on the GPU; the oracle
+    runs two heads of different groups over all sequences, which fixes their dx,
+    ddt, dinit, dA and dD."""
+    inp = wl.workload_inputs(3)
+    rng = np.random.default_rng(303)
+    b, L, H, P = inp["x"].shape
+    N = inp["B"].shape[3]
+    inp["dy"] = wl._round_io(rng.standard_normal((b, L, H, P), dtype=np.float32), "bf16")
+    inp["dfinal"] = rng.standard_normal((inp["nseq"], H, P, N)).astype(np.float32)
+    got = _gpu(inp)
+    heads = [1, 30]   # groups 0 and 7
+    mask = np.zeros((inp["nseq"], H), dtype=bool)
+    mask[:, heads] = True
+    ref = _ref(inp, unit_mask=mask)
+    errs = {}
+    for k, axis in (("dx", 2), ("ddt", 2), ("dinit", 1)):
+        g = np.take(hp.to_numpy64(got[k]), heads, axis=axis)
+        errs[k] = hp.rel_l2(g, np.take(ref[k], heads, axis=axis))
+    for k in ("dA", "dD"):
+        errs[k] = hp.rel_l2(hp.to_numpy64(got[k])[heads], ref[k][heads])
+    print("[bwd varlen full] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= 1e-2, (k, v)
