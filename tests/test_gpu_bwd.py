@@ -69,6 +69,27 @@ def test_backward_small(io, b, L, H, P, N, G, lengths):
         assert v <= tol, (k, v)
 
 
+@pytest.mark.parametrize("io,P,N", [("bf16", 64, 128), ("bf16", 32, 32), ("f32", 32, 32)])
+def test_backward_degenerate_decay_and_steps(io, P, N):
+    """A = 0 on one head (no decay: the linear-attention limit), a run of dt = 0
+    tokens across a chunk boundary (no update, unit decay), no D, no initial
+    state and no final-state gradient."""
+    inp = _inputs(io, 1, 190, 3, P, N, 1, seed=77, init=False)
+    inp["A"] = inp["A"].copy()
+    inp["A"][1] = 0.0
+    inp["dt"] = inp["dt"].copy()
+    inp["dt"][0, 50:80, :] = 0.0
+    inp["D"] = None
+    inp["dfinal"] = None
+    got, ref = _gpu(inp), _ref(inp)
+    errs = {k: hp.rel_l2(hp.to_numpy64(got[k]), ref[k]) for k in GRADS}
+    print(f"[bwd degenerate] {io} P{P} N{N} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= hp.TOL[io], (k, v)
+    # no update on the dt = 0 tokens: their dx is only the (absent) skip term
+    assert np.all(hp.to_numpy64(got["dx"])[0, 50:80] == 0.0)
+
+
 def test_backward_deterministic():
     inp = _inputs("bf16", 2, 300, 4, 64, 128, 1, seed=3)
     a, b = _gpu(inp), _gpu(inp)
