@@ -20,6 +20,11 @@
 //             + exp(s_last - s_j) (X R_c)_j . B_j,   dA = sum_j dt_j dL/da_j,
 //   dD = sum dY . X,   dinit = R_{-1}.
 //
+// <R_c, H_{c+1}> is evaluated as exp(s_last) <R_c, H_c> + sum_j w_j (X R_c)_j . B_j
+// (H_{c+1} expanded by one chunk of the recurrence), so that H_{c+1} is not
+// read and its chunk-state part is built from the same products as the
+// -w_i (X R_c)_i . B_i terms it cancels against.
+//
 // Kernels: ssd_bwd_prep_kernel (chunk table), ssd_bwd_scan_kernel (forward
 // boundary states H_c, or the reverse chain R_c; one workgroup per
 // (sequence, head), chunk-sequential), ssd_bwd_chunk_kernel (everything
