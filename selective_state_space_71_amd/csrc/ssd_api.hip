@@ -587,6 +587,9 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
     const long long want = 8LL * cus;
     long long hs = (w.max_entries * d.nheads + want - 1) / want;
     hs = hs < 1 ? 1 : (hs > hpg ? hpg : hs);
+    // but at least two heads where the group has them: an item's set-up (its
+    // B chunk into LDS, the C B^T tiles) costs about as much as one head
+    if (hs < 2 && hpg >= 2) hs = 2;
     const int slices = (int)((hpg + hs - 1) / hs);
     pp.G = d.ngroups;
     pp.slices = slices;
