@@ -35,6 +35,10 @@
  *   - Preconditions that are documented but not checked: inputs are finite;
  *     cu_seqlens[0] == 0, cu_seqlens is non-decreasing and its last entry is
  *     seqlen.  Non-finite values stay inside their own sequence.
+ *   - With the environment variable SSD_DEBUG_VALIDATE=1, every entry point
+ *     that takes cu_seqlens copies it to the host first (this synchronises
+ *     `stream`, so not under graph capture) and returns SSD_ERR_SHAPE,
+ *     launching nothing, when it breaks the precondition above.
  */
 #ifndef SSD_H
 #define SSD_H

@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 #include <utility>
+#include <vector>
 
 #include "ssd.h"
 #include "ssd_device.h"
@@ -401,6 +404,23 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Optional check of the packed-sequence offsets, enabled by the environment
+// variable SSD_DEBUG_VALIDATE=1: copies them to the host (which synchronises
+// `s`) and requires cu[0] == 0, non-decreasing entries and cu[nseq] ==
+// seqlen.  Without the variable these are unchecked preconditions.
+ssd_status_t debug_check_cu_seqlens(const int32_t *cu, int nseq, int seqlen, hipStream_t s) {
+    const char *flag = std::getenv("SSD_DEBUG_VALIDATE");
+    if (!cu || !flag || std::strcmp(flag, "1") != 0) return SSD_OK;
+    std::vector<int32_t> h((size_t)nseq + 1);
+    if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SSD_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SSD_ERR_HIP;
+    if (h[0] != 0 || h[(size_t)nseq] != seqlen) return SSD_ERR_SHAPE;
+    for (int i = 0; i < nseq; ++i)
+        if (h[(size_t)i + 1] < h[(size_t)i]) return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+
 struct WsLayout {
     size_t flags, chunks, items, scratch, state, total;
     long long max_entries;
@@ -559,6 +579,8 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
 
     char *ws = static_cast<char *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu_seqlens(cu_seqlens, d.nseq, d.seqlen, s);
+    if (st != SSD_OK) return st;
     ssd::PrepParams pp{};
     pp.cu_seqlens = cu_seqlens;
     pp.batch = d.batch;
@@ -735,6 +757,9 @@ ssd_status_t ssd_causal_conv1d_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32
     if (overlap(rx, rB) || overlap(rx, rC) || overlap(rB, rC) || overlap(rso, rx) || overlap(rso, rB) ||
         overlap(rso, rC))
         return SSD_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const ssd_status_t cst = debug_check_cu_seqlens(cu_seqlens, d.nseq, d.seqlen, st);
+    if (cst != SSD_OK) return cst;
     ssd::ConvParams p{};
     p.xbc = xbc;
     p.w = weight;
@@ -757,7 +782,6 @@ ssd_status_t ssd_causal_conv1d_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32
     while ((tokens + run * 4 - 1) / (run * 4) > 65535) run *= 2;
     p.run = (int)run;
     const dim3 grid((unsigned)((Cc / 8 + 63) / 64), (unsigned)((tokens + run * 4 - 1) / (run * 4)));
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const bool ok = (io == SSD_BF16) ? ssd::conv_launch<ssd::bf16>(width, p, grid, st)
                                      : ssd::conv_launch<float>(width, p, grid, st);
     if (!ok) return SSD_ERR_UNSUPPORTED;
@@ -896,6 +920,8 @@ ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const vo
 
     char *ws = static_cast<char *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu_seqlens(cu_seqlens, d.nseq, d.seqlen, s);
+    if (st != SSD_OK) return st;
     ssd::BwdPrepParams pp{};
     pp.cu_seqlens = cu_seqlens;
     pp.batch = d.batch;

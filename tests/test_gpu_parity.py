@@ -61,6 +61,10 @@ def _check_fwd(inp, chunk_len, tol=None, tag=""):
     (1, 1000, 8, 64, 128, 4, 128, True),
     (3, 64, 2, 64, 32, 1, 64, True),
     (1, 1, 2, 64, 128, 1, 256, True),
+    # one head per group (one-head work items), and five heads per group
+    # (two-head slices with a one-head remainder)
+    (2, 500, 4, 64, 128, 4, 128, True),
+    (1, 600, 5, 64, 128, 1, 256, True),
     # the larger head and state dims
     (1, 300, 2, 128, 128, 1, 128, True),
     (2, 200, 2, 64, 256, 1, 128, True),
@@ -152,6 +156,48 @@ def test_varlen_matches_oracle_and_per_sequence_calls():
                                     d["D"], chunk_len=128, init_state=d["init_state"][s:s + 1].contiguous())
         assert torch.equal(ys, y[:, lo:hi]), s                 # same chunking -> same bits
         assert torch.equal(fs, fin[s:s + 1]), s
+
+
+def test_debug_validation_of_cu_seqlens(monkeypatch):
+    """SSD_DEBUG_VALIDATE=1: malformed packed-sequence offsets are rejected
+    before anything is launched by the forward, the backward and the
+    convolution prologue; well-formed offsets give the same bits as without
+    the check.  (Every malformed case here also stays inside the buffers and
+    the workspace's chunk table, should a call go through.)"""
+    T = 300
+    inp = wl.make_inputs(1, T, 2, 64, 128, 1, io="bf16", seed=41, init_std=0.3, lengths=[120, 100, 80])
+    d = hp.to_device(inp, DEV)
+    dy = torch.randn(d["x"].shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    Cc = 2 * 64 + 2 * 128
+    xbc = torch.randn((1, T, Cc), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16).to(DEV)
+    wconv = torch.randn((Cc, 4), generator=torch.Generator().manual_seed(7)).to(DEV)
+
+    def calls(cu):
+        y, fin = ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk_len=64,
+                                    init_state=d["init_state"], cu_seqlens=cu)
+        g = ssd.chunk_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dy, D=d["D"],
+                               init_state=d["init_state"], cu_seqlens=cu)
+        conv = ssd.causal_conv1d_fwd(xbc, wconv, 2, 64, 1, 128, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        return [y, fin, *g.values(), *conv]
+
+    good = d["cu_seqlens"]
+    plain = calls(good)
+    monkeypatch.setenv("SSD_DEBUG_VALIDATE", "1")
+    checked = calls(good)
+    for a, b in zip(plain, checked):
+        assert torch.equal(a, b)
+    bad_cases = ([0, 200, 100, 300],   # decreasing
+                 [10, 100, 200, 300],  # does not start at 0
+                 [0, 100, 200, 250])   # does not end at seqlen
+    for bad in bad_cases:
+        cu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        with pytest.raises(ssd.SsdError, match="SSD_ERR_SHAPE"):
+            ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk_len=64, cu_seqlens=cu)
+        with pytest.raises(ssd.SsdError, match="SSD_ERR_SHAPE"):
+            ssd.chunk_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dy, D=d["D"], cu_seqlens=cu)
+        with pytest.raises(ssd.SsdError, match="SSD_ERR_SHAPE"):
+            ssd.causal_conv1d_fwd(xbc, wconv, 2, 64, 1, 128, cu_seqlens=cu)
 
 
 def test_varlen_nan_stays_in_its_sequence():
