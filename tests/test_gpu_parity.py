@@ -117,6 +117,60 @@ def test_chunk_len_invariance_fp32():
         _check_fwd(inp, q, tag="invariance f32")
 
 
+# ------------------------------------------------------------------ stage pins
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_stage_pins(io):
+    """The stages of the fused forward against the oracle one at a time.
+
+    - Chunk-local output (in-chunk cumsum and diagonal blocks): the batch
+      repacked so that every chunk is a sequence of its own, with no initial
+      state and no D, so the GPU output is Y_diag alone; the reference is the
+      oracle recurrence restarted at every chunk start.
+    - Boundary states (chunk states and the recurrence): the final states of
+      runs over the first c chunks against the oracle's state after those
+      tokens, c = 1 .. all (the last chunk is ragged).
+    - Read-out: Y_off = y - Y_diag (D = 0) against the oracle's difference;
+      fp32 io only, since the difference of two bf16-rounded outputs does not
+      resolve Y_off to 1e-2.
+    """
+    Q, b, H, P, N = 64, 2, 2, 64, 64
+    L = 5 * Q - 17
+    nc = -(-L // Q)
+    inp = wl.make_inputs(b, L, H, P, N, 1, io=io, seed=51, init_std=0.5)
+    tol = hp.TOL[io]
+    d = hp.to_device(inp, DEV)
+
+    starts = [s * L + c * Q for s in range(b) for c in range(nc)]
+    flat = lambda a: np.ascontiguousarray(a.reshape((1, b * L) + a.shape[2:]))
+    packed = dict(inp, x=flat(inp["x"]), dt=flat(inp["dt"]), B=flat(inp["B"]), C=flat(inp["C"]),
+                  init_state=None, cu_seqlens=np.array(starts + [b * L], dtype=np.int32))
+    pd = hp.to_device(packed, DEV)
+    y_diag, _ = ssd.chunk_scan_fwd(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], None, chunk_len=Q,
+                                   cu_seqlens=pd["cu_seqlens"])
+    y_diag = hp.to_numpy64(y_diag).reshape(b, L, H, P)
+    y_diag_ref = hp.oracle_fwd(packed, D=False, init=False)[0].reshape(b, L, H, P)
+    err = hp.rel_l2(y_diag, y_diag_ref)
+    assert err <= tol, f"Y_diag {err:.2e}"
+
+    for c in range(1, nc + 1):
+        n = min(c * Q, L)
+        pre = dict(inp, x=inp["x"][:, :n], dt=inp["dt"][:, :n], B=inp["B"][:, :n], C=inp["C"][:, :n])
+        pg = hp.to_device(pre, DEV)
+        _, fin = ssd.chunk_scan_fwd(pg["x"], pg["dt"], pg["A"], pg["B"], pg["C"], None, chunk_len=Q,
+                                    init_state=pg["init_state"])
+        fin_ref = hp.oracle_fwd(pre, D=False)[1]
+        err = hp.rel_l2(hp.to_numpy64(fin), fin_ref)
+        assert err <= tol, f"H_{c} {err:.2e}"
+
+    if io == "f32":
+        y, _ = ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], None, chunk_len=Q,
+                                  init_state=d["init_state"])
+        y_off = hp.to_numpy64(y) - y_diag
+        y_off_ref = hp.oracle_fwd(inp, D=False)[0] - y_diag_ref
+        err = hp.rel_l2(y_off, y_off_ref)
+        assert err <= tol, f"Y_off {err:.2e}"
+
+
 # ------------------------------------------------------------------ worked example
 def test_scalar_gate_on_gpu():
     """Feghi's Mamba review, section 3: 10 and 2 -> 9.2 (g=0.1), 2.8 (g=0.9),
