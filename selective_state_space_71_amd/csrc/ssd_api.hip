@@ -2,6 +2,7 @@
 // layout, the chunk-schedule kernel, the decode kernel and the C ABI.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstddef>
@@ -377,25 +378,30 @@ bool overlap(Range a, Range b) {
 }
 
 // A device attribute of the current device (cached per device id), or -1.
-int device_attr(hipDeviceAttribute_t attr, int (&cache)[64]) {
+// The cache only ever holds the attribute's value, so concurrent first calls
+// store the same number; the accesses are atomic to keep that race defined.
+int device_attr(hipDeviceAttribute_t attr, std::atomic<int> (&cache)[64]) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, attr, dev) != hipSuccess || n <= 0) return -1;
-    if (dev >= 0 && dev < 64) cache[dev] = n;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
 int num_compute_units() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64] = {};
     return device_attr(hipDeviceAttributeMultiprocessorCount, cache);
 }
 
 // Number of XCDs (accelerator complexes, each with its own L2) of the
 // current device, clamped to [1, 16].
 int num_xcds() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64] = {};
     const int n = device_attr(hipDeviceAttributeNumberOfXccs, cache);
     return n < 1 ? 1 : (n > 16 ? 16 : n);
 }
