@@ -90,6 +90,18 @@ def test_backward_degenerate_decay_and_steps(io, P, N):
     assert np.all(hp.to_numpy64(got["dx"])[0, 50:80] == 0.0)
 
 
+def test_backward_many_short_sequences():
+    """A packed batch of 4,500 sequences of 0 to 40 tokens (more chunks than
+    sequences of any earlier case, most of them single partial chunks)."""
+    rng = np.random.default_rng(63)
+    lens = [int(v) for v in rng.integers(0, 41, size=4500)]
+    inp = _inputs("bf16", 1, sum(lens), 2, 64, 64, 1, seed=64, lengths=lens)
+    got, ref = _gpu(inp), _ref(inp)
+    for k in GRADS:
+        err = hp.rel_l2(hp.to_numpy64(got[k]), ref[k])
+        assert err <= hp.TOL["bf16"], (k, err)
+
+
 def test_backward_deterministic():
     inp = _inputs("bf16", 2, 300, 4, 64, 128, 1, seed=3)
     a, b = _gpu(inp), _gpu(inp)

@@ -254,6 +254,17 @@ def test_debug_validation_of_cu_seqlens(monkeypatch):
             ssd.causal_conv1d_fwd(xbc, wconv, 2, 64, 1, 128, cu_seqlens=cu)
 
 
+def test_varlen_many_short_sequences():
+    """A packed batch of 4,500 sequences of 0 to 40 tokens: more chunk entries
+    than the schedule kernel caches per entry (4,096), with one group and one
+    head slice, so the per-XCD item lists take their general (ballot) path."""
+    rng = np.random.default_rng(61)
+    lens = [int(v) for v in rng.integers(0, 41, size=4500)]
+    inp = wl.make_inputs(1, sum(lens), 2, 64, 64, 1, io="bf16", seed=62, init_std=0.3, lengths=lens)
+    assert sum(1 for v in lens if v > 0) > 4096
+    _check_fwd(inp, 64, tag="4500 short sequences")
+
+
 def test_varlen_nan_stays_in_its_sequence():
     lens = [200, 300, 100]
     inp = wl.make_inputs(1, 600, 2, 64, 128, 1, io="bf16", seed=22, lengths=lens)
