@@ -102,6 +102,18 @@ def test_backward_many_short_sequences():
         assert err <= hp.TOL["bf16"], (k, err)
 
 
+def test_backward_maximum_sequence_count():
+    """65,536 packed sequences (0 to 2 tokens each, one of 300 tokens)."""
+    rng = np.random.default_rng(67)
+    lens = [int(v) for v in rng.integers(0, 3, size=65536)]
+    lens[4321] = 300
+    inp = _inputs("bf16", 1, sum(lens), 2, 32, 32, 1, seed=68, lengths=lens)
+    got, ref = _gpu(inp), _ref(inp)
+    for k in GRADS:
+        err = hp.rel_l2(hp.to_numpy64(got[k]), ref[k])
+        assert err <= hp.TOL["bf16"], (k, err)
+
+
 def test_backward_deterministic():
     inp = _inputs("bf16", 2, 300, 4, 64, 128, 1, seed=3)
     a, b = _gpu(inp), _gpu(inp)

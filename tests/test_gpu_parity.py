@@ -265,6 +265,16 @@ def test_varlen_many_short_sequences():
     _check_fwd(inp, 64, tag="4500 short sequences")
 
 
+def test_varlen_maximum_sequence_count():
+    """The largest packed batch the entry point accepts: 65,536 sequences
+    (0 to 2 tokens each, one of 300 tokens)."""
+    rng = np.random.default_rng(65)
+    lens = [int(v) for v in rng.integers(0, 3, size=65536)]
+    lens[777] = 300
+    inp = wl.make_inputs(1, sum(lens), 2, 32, 32, 1, io="bf16", seed=66, init_std=0.3, lengths=lens)
+    _check_fwd(inp, 128, tag="65536 sequences")
+
+
 def test_varlen_nan_stays_in_its_sequence():
     lens = [200, 300, 100]
     inp = wl.make_inputs(1, 600, 2, 64, 128, 1, io="bf16", seed=22, lengths=lens)
