@@ -275,6 +275,13 @@ def test_varlen_maximum_sequence_count():
     _check_fwd(inp, 128, tag="65536 sequences")
 
 
+def test_long_single_sequence():
+    """One sequence of 262,144 tokens: a chain of 1,024 chunk hand-offs per
+    head, each waiting on its predecessor's published state."""
+    inp = wl.make_inputs(1, 262144, 2, 64, 128, 1, io="bf16", seed=71, init_std=0.3)
+    _check_fwd(inp, 256, tag="L=262144")
+
+
 def test_varlen_nan_stays_in_its_sequence():
     lens = [200, 300, 100]
     inp = wl.make_inputs(1, 600, 2, 64, 128, 1, io="bf16", seed=22, lengths=lens)
