@@ -65,6 +65,7 @@ def _check_fwd(inp, chunk_len, tol=None, tag=""):
     # (two-head slices with a one-head remainder)
     (2, 500, 4, 64, 128, 4, 128, True),
     (1, 600, 5, 64, 128, 1, 256, True),
+    (1, 333, 1, 64, 128, 1, 128, True),
     # the larger head and state dims
     (1, 300, 2, 128, 128, 1, 128, True),
     (2, 200, 2, 64, 256, 1, 128, True),
@@ -331,6 +332,26 @@ def test_zero_step_keeps_state():
     torch.cuda.synchronize()
     assert torch.equal(fin, d["init_state"])
     _check_fwd(inp, 128, tag="dt=0")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_extreme_decay(io):
+    """A = -1e4 (every decay, and the factorized mask's both factors, below
+    fp32's range after one token), A = 0 (no decay at all: causal linear
+    attention) and an ordinary head in one call; finite outputs that match
+    the oracle."""
+    inp = wl.make_inputs(2, 500, 3, 64, 64, 1, io=io, seed=27, init_std=0.5)
+    inp["A"] = np.array([-1e4, 0.0, inp["A"][2]], dtype=np.float32)
+    _check_fwd(inp, 128, tag=f"extreme decay {io}")
+    # per head as well: the undecayed head dominates the whole tensor's norm
+    d = hp.to_device(inp, DEV)
+    y, fin = _run(d, 128, D=False)
+    y_ref, fin_ref = hp.oracle_fwd(inp, D=False)
+    y, fin = hp.to_numpy64(y), hp.to_numpy64(fin)
+    for h in range(3):
+        ey = hp.rel_l2(y[:, :, h], y_ref[:, :, h])
+        ef = hp.rel_l2(fin[:, h], fin_ref[:, h])
+        assert ey <= hp.TOL[io] and ef <= hp.TOL[io], (h, ey, ef)
 
 
 def test_run_to_run_bitwise_deterministic():
