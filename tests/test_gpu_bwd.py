@@ -114,6 +114,25 @@ def test_backward_maximum_sequence_count():
         assert err <= hp.TOL["bf16"], (k, err)
 
 
+@pytest.mark.parametrize("io,P,N", [("bf16", 64, 64), ("f32", 32, 32)])
+def test_backward_extreme_decay(io, P, N):
+    """A = -1e4 (every decay below fp32's range within a token), A = 0 and an
+    ordinary head in one call.  Gradients indexed by head are compared per
+    head (the undecayed head dominates every norm), dB and dC as a whole."""
+    inp = _inputs(io, 2, 300, 3, P, N, 1, seed=81)
+    inp["A"] = np.array([-1e4, 0.0, inp["A"][2]], dtype=np.float32)
+    got, ref = _gpu(inp), _ref(inp)
+    tol = hp.TOL[io]
+    g = {k: hp.to_numpy64(got[k]) for k in GRADS}
+    for k in ("dB", "dC"):
+        assert hp.rel_l2(g[k], ref[k]) <= tol, k
+    for h in range(3):
+        for k, sl in (("dx", np.s_[:, :, h]), ("ddt", np.s_[:, :, h]), ("dinit", np.s_[:, h])):
+            assert hp.rel_l2(g[k][sl], ref[k][sl]) <= tol, (k, h)
+        for k in ("dA", "dD"):
+            assert abs(g[k][h] - ref[k][h]) <= tol * max(abs(ref[k][h]), 1e-30), (k, h, g[k][h], ref[k][h])
+
+
 def test_backward_deterministic():
     inp = _inputs("bf16", 2, 300, 4, 64, 128, 1, seed=3)
     a, b = _gpu(inp), _gpu(inp)
