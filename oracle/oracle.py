@@ -257,7 +257,10 @@ def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal
 
     Shapes as for ssd_fwd; dy like y, dfinal like final_state (or None).
     Returns a dict with dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC
-    [b, L, G, N], dD [H] and dinit [nseq, H, P, N].  ``unit_mask`` [nseq, H]
+    [b, L, G, N], dD [H] and dinit [nseq, H, P, N], plus dA_abs [H]: the sum
+    of the absolute values of dA's per-token terms dt_t <dL/dh_t, abar_t
+    h_{t-1}>, the scale against which dA's rounding error is measured (its
+    terms can cancel).  ``unit_mask`` [nseq, H]
     (bool) restricts the work to some (sequence, head) pairs: the other pairs'
     gradients stay zero, and dB, dC, dA, dD sum the chosen pairs only."""
     x = _f64(x); dt = _f64(dt); A = _f64(A); B = _f64(B); C = _f64(C); dy = _f64(dy)
@@ -275,7 +278,7 @@ def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal
     init = np.zeros((nseq, H, P, N)) if init_state is None else _f64(init_state)
     dfin = np.zeros((nseq, H, P, N)) if dfinal is None else _f64(dfinal)
     out = dict(dx=np.zeros_like(x), ddt=np.zeros_like(dt), dA=np.zeros(H), dB=np.zeros_like(B),
-               dC=np.zeros_like(C), dD=np.zeros(H), dinit=np.zeros((nseq, H, P, N)))
+               dC=np.zeros_like(C), dD=np.zeros(H), dinit=np.zeros((nseq, H, P, N)), dA_abs=np.zeros(H))
     for s, (bi, a, e) in enumerate(spans):
         for h in range(H):
             if unit_mask is not None and not unit_mask[s][h]:
@@ -300,6 +303,7 @@ def ssd_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None, dfinal
                 q = float(np.sum(g * (abar * hs[i])))
                 out["ddt"][bi, t, h] += float(x[bi, t, h] @ gB) + A[h] * q
                 out["dA"][h] += dt[bi, t, h] * q
+                out["dA_abs"][h] += abs(dt[bi, t, h] * q)
                 out["dD"][h] += float(dy[bi, t, h] @ x[bi, t, h])
                 g = abar * g                                            # dL/dh_{t-1}
             out["dinit"][s, h] = g

@@ -212,8 +212,10 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None
         _need(final_state, "final_state", torch.float32, (nseq, H, P, N), dev)
     ws_bytes = workspace_size(dims, chunk_len, io)
     if ws_bytes == 0:
-        code = lib.ssd_chunk_scan_fwd(ctypes.byref(dims), io, chunk_len, *([None] * 10),
-                                      None, 0, None)
+        # the call itself names the reason (shape checks come before pointer
+        # checks); cu_seqlens decides between the dense and the packed rules
+        code = lib.ssd_chunk_scan_fwd(ctypes.byref(dims), io, chunk_len, *([None] * 7), _ptr(cu_seqlens),
+                                      None, None, None, 0, None)
         raise SsdError(code, "ssd_chunk_scan_fwd (size query)")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -370,7 +372,8 @@ def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, cu_seqlens=None,
                dD=torch.empty(H, **f32), dinit=torch.empty((nseq, H, P, N), **f32) if want_dinit else None)
     n = int(lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(dims), io))
     if n == 0:
-        code = lib.ssd_chunk_scan_bwd(ctypes.byref(dims), io, *([None] * 18), 0, None)
+        code = lib.ssd_chunk_scan_bwd(ctypes.byref(dims), io, *([None] * 7), _ptr(cu_seqlens), *([None] * 10),
+                                      0, None)
         raise SsdError(code, "ssd_chunk_scan_bwd (size query)")
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)

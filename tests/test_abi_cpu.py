@@ -113,6 +113,10 @@ def test_varlen_validation(lib):
     assert _fwd(lib, _dims(), cu=FAKE + (20 << 30)) == 2
     # and nseq <= 65536
     assert _fwd(lib, _dims(batch=1, nseq=70000), cu=FAKE + (20 << 30)) == 2
+    # a packed batch whose tiles do not fit is reported as unsupported, not
+    # as a layout error (the binding relies on this to name the reason)
+    assert _fwd(lib, _dims(batch=1, nseq=5, headdim=128, dstate=128), io=ssd.SSD_F32,
+                cu=FAKE + (20 << 30)) == 4
 
 
 def _dec(lib, dims, io=ssd.SSD_BF16, **ptrs):

@@ -283,6 +283,19 @@ def test_long_single_sequence():
     _check_fwd(inp, 256, tag="L=262144")
 
 
+def test_unsupported_packed_shape_is_named():
+    """A packed fp32 batch whose chunk tiles exceed LDS (head dim 128, state
+    128, chunk 256) raises SSD_ERR_UNSUPPORTED, forward and backward."""
+    inp = wl.make_inputs(1, 300, 2, 128, 128, 1, io="f32", seed=29, lengths=[100, 200])
+    d = hp.to_device(inp, DEV)
+    with pytest.raises(ssd.SsdError, match="SSD_ERR_UNSUPPORTED"):
+        ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk_len=256,
+                           cu_seqlens=d["cu_seqlens"])
+    with pytest.raises(ssd.SsdError, match="SSD_ERR_UNSUPPORTED"):
+        ssd.chunk_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["x"].clone(), D=d["D"],
+                           cu_seqlens=d["cu_seqlens"])
+
+
 def test_varlen_nan_stays_in_its_sequence():
     lens = [200, 300, 100]
     inp = wl.make_inputs(1, 600, 2, 64, 128, 1, io="bf16", seed=22, lengths=lens)

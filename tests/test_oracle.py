@@ -495,6 +495,41 @@ def test_backward_matches_finite_differences(kw):
         np.testing.assert_allclose(g[gk], fd, rtol=1e-6, atol=1e-7, err_msg=k)
 
 
+def test_backward_dA_term_scale():
+    """dA_abs (the sum over tokens of |dt_t <dL/dh_t, abar_t h_{t-1}>|, the
+    scale of dA's rounding error) bounds |dA| and equals it for a one-token
+    sequence (a single term).  With two tokens, each term is measured on its
+    own by finite differences: scaling dt_t by (1 + e) while x_t is scaled by
+    1 / (1 + e) leaves the input dt_t x_t B_t unchanged (D = 0) and moves only
+    a_t = dt_t A, by e dt_t A, so the difference quotient is A times the term."""
+    p, cu, dy, dfin = _bwd_problem(33, L=12)
+    g = oracle.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], dy, D=p["D"], init_state=p["init_state"],
+                       dfinal=dfin)
+    assert np.all(g["dA_abs"] >= np.abs(g["dA"]) * (1 - 1e-12))
+    p1, _, dy1, dfin1 = _bwd_problem(34, L=1)
+    g1 = oracle.ssd_bwd(p1["x"], p1["dt"], p1["A"], p1["B"], p1["C"], dy1, D=p1["D"],
+                        init_state=p1["init_state"], dfinal=dfin1)
+    np.testing.assert_allclose(g1["dA_abs"], np.abs(g1["dA"]), rtol=1e-13)
+    # two tokens: each term is the dA of the loss restricted to one token's
+    # decay, i.e. dt_t times the derivative with respect to a_t = dt_t A
+    p2, _, dy2, dfin2 = _bwd_problem(35, L=2)
+    p2["D"] = np.zeros_like(p2["D"])
+    g2 = oracle.ssd_bwd(p2["x"], p2["dt"], p2["A"], p2["B"], p2["C"], dy2, D=p2["D"],
+                        init_state=p2["init_state"], dfinal=dfin2)
+    eps = 1e-6
+    terms = np.zeros((2, p2["A"].size))
+    for h in range(p2["A"].size):
+        for t in range(2):
+            q = dict((k, v.copy()) for k, v in p2.items())
+            lp = []
+            for sgn in (1, -1):
+                q["dt"][0, t, h] = p2["dt"][0, t, h] * (1 + sgn * eps)
+                q["x"][0, t, h] = p2["x"][0, t, h] / (1 + sgn * eps)
+                lp.append(_loss(q, None, dy2, dfin2))
+            terms[t, h] = (lp[0] - lp[1]) / (2 * eps) / p2["A"][h]
+    np.testing.assert_allclose(g2["dA_abs"], np.abs(terms).sum(axis=0), rtol=1e-6)
+
+
 def test_backward_euler_identities():
     """y and final_state are jointly linear in (x, init) and linear in B and in
     C, so the gradient contracted with the input returns the loss exactly."""
