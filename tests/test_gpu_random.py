@@ -1,0 +1,127 @@
+"""Seeded randomized parity against the fp64 oracle: a fixed draw of shapes
+(head and state dims, chunk lengths, groups, dense and packed batches, initial
+states, both io dtypes) through the forward, the backward, the decode step and
+the block prologue and epilogue.  Same tolerances as the other GPU tests; dA,
+a sum over every token whose terms can cancel, is held to 64 ulps of its term
+scale (the oracle's dA_abs) where that is the looser bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from selective_state_space_71_amd import ssd
+from selective_state_space_71_amd import workloads as wl
+from tests import helpers as hp
+from tests.test_gpu_bwd import GRADS, _gpu, _inputs, _ref
+from tests.test_gpu_block import _conv_gpu, _conv_ref, _split_ref
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+EPS = {"f32": float(np.finfo(np.float32).eps), "bf16": 2.0 ** -8}
+
+
+def _lengths(rng, hi):
+    lens = [int(v) for v in rng.integers(0, hi, size=int(rng.integers(1, 6)))]
+    if sum(lens) == 0:
+        lens[0] = 5
+    return lens
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_forward_and_backward(seed):
+    rng = np.random.default_rng(9000 + seed)
+    done = 0
+    while done < 12:
+        io = str(rng.choice(["bf16", "f32"]))
+        P = int(rng.choice([16, 32, 64, 128]))
+        N = int(rng.choice([16, 32, 64, 128, 256]))
+        Q = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2]))
+        H = G * int(rng.integers(1, 4))
+        lens = _lengths(rng, 300) if rng.random() < 0.4 else None
+        b, L = (1, sum(lens)) if lens else (int(rng.integers(1, 3)), int(rng.integers(1, 700)))
+        init = bool(rng.random() < 0.7)
+        inp = wl.make_inputs(b, L, H, P, N, G, io=io, seed=int(rng.integers(1 << 30)),
+                             init_std=0.5 if init else None, lengths=lens)
+        tag = f"{io} b{b} L{L} H{H} P{P} N{N} G{G} Q{Q} lens={lens} init={init}"
+        d = hp.to_device(inp, DEV)
+        try:
+            y, fin = ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], None, chunk_len=Q,
+                                        init_state=d["init_state"], cu_seqlens=d["cu_seqlens"])
+        except ssd.SsdError as e:
+            assert "SSD_ERR_UNSUPPORTED" in str(e), (tag, str(e))
+            continue
+        torch.cuda.synchronize()
+        assert ssd.check_workspace(ssd.chunk_scan_fwd.last_workspace) == 0
+        y_ref, fin_ref = hp.oracle_fwd(inp, D=False)
+        assert hp.rel_l2(hp.to_numpy64(y), y_ref) <= hp.TOL[io], tag
+        assert hp.rel_l2(hp.to_numpy64(fin), fin_ref) <= hp.TOL[io], tag
+        done += 1
+        if P <= 64 and N <= (128 if io == "bf16" else 64):
+            binp = _inputs(io, b, L, H, P, N, G, seed=int(rng.integers(1 << 30)), lengths=lens, init=init)
+            got, ref = _gpu(binp), _ref(binp)
+            for k in GRADS:
+                g = hp.to_numpy64(got[k])
+                if hp.rel_l2(g, ref[k]) <= hp.TOL[io]:
+                    continue
+                assert k == "dA", (tag, k, hp.rel_l2(g, ref[k]))
+                assert np.all(np.abs(g - ref[k]) <= 64 * EPS[io] * ref["dA_abs"]), (tag, g, ref[k])
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_decode(seed):
+    rng = np.random.default_rng(9100 + seed)
+    for _ in range(25):
+        io = str(rng.choice(["bf16", "f32"]))
+        H = int(rng.integers(1, 5))
+        G = int(rng.choice([g for g in (1, 2, 4) if H % g == 0]))
+        P, N, b = int(rng.integers(1, 130)), int(rng.choice([16, 32, 64, 128, 256])), int(rng.integers(1, 9))
+        di = wl.make_decode_inputs(b, H, P, N, G, io=io, seed=int(rng.integers(1 << 30)))
+        st = hp.f32_tensor(di["state"], DEV)
+        y = ssd.decode_step(st, hp.io_tensor(di["x"], io, DEV), hp.f32_tensor(di["dt"], DEV),
+                            hp.f32_tensor(di["A"], DEV), hp.io_tensor(di["B"], io, DEV),
+                            hp.io_tensor(di["C"], io, DEV), hp.f32_tensor(di["D"], DEV))
+        torch.cuda.synchronize()
+        y_ref, st_ref = hp.oracle_decode(di)
+        tag = f"{io} b{b} H{H} P{P} N{N} G{G}"
+        assert hp.rel_l2(hp.to_numpy64(y), y_ref) <= hp.TOL[io], tag
+        assert hp.rel_l2(hp.to_numpy64(st), st_ref) <= hp.TOL[io], tag
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_block_kernels(seed):
+    rng = np.random.default_rng(9200 + seed)
+    for _ in range(25):
+        io = str(rng.choice(["bf16", "f32"]))
+        H = int(rng.integers(1, 5))
+        P, N = int(rng.choice([8, 16, 32, 64])), int(rng.choice([8, 16, 32, 64, 128]))
+        G = int(rng.choice([g for g in (1, 2) if H % g == 0]))
+        W = int(rng.integers(1, 5))
+        lens = _lengths(rng, 200) if rng.random() < 0.4 else None
+        b, L = (1, sum(lens)) if lens else (int(rng.integers(1, 3)), int(rng.integers(1, 400)))
+        state, silu, bias = (bool(rng.random() < p) for p in (0.6, 0.7, 0.7))
+        d = wl.make_block_inputs(b, L, H, P, N, G, W, io, seed=int(rng.integers(1 << 30)), lengths=lens,
+                                 with_state=state)
+        x, B, C, so = _conv_gpu(d, silu=silu, bias=bias, state=state)
+        out_ref, fin_ref = _conv_ref(d, silu=silu, bias=bias, state=state)
+        tag = f"conv {io} b{b} L{L} H{H} P{P} N{N} G{G} W{W} lens={lens}"
+        for got, ref in zip((x, B, C), _split_ref(out_ref, d)):
+            assert hp.rel_l2(hp.to_numpy64(got), ref) <= hp.TOL[io], tag
+        np.testing.assert_array_equal(hp.to_numpy64(so), fin_ref)
+
+        rows = int(rng.integers(1, 300))
+        dim = int(rng.choice([16, 48, 64, 256, 640, 1024] + ([5120] if io == "bf16" else [])))
+        gs = int(rng.choice([g for g in (8, 16, 48, 64, 128, 256, 640, 1024, 5120) if dim % g == 0]))
+        gate, before = bool(rng.random() < 0.7), bool(rng.random() < 0.4)
+        eps = float(rng.choice([1e-5, 1e-6, 1e-3]))
+        r = np.random.default_rng(int(rng.integers(1 << 30)))
+        yv = wl._round_io(r.standard_normal((rows, dim), dtype=np.float32), io)
+        zv = wl._round_io(r.standard_normal((rows, dim), dtype=np.float32), io)
+        w = r.standard_normal(dim).astype(np.float32)
+        out = ssd.gated_rmsnorm_fwd(hp.io_tensor(yv, io, DEV), hp.io_tensor(zv, io, DEV) if gate else None,
+                                    hp.f32_tensor(w, DEV), eps=eps, group_size=gs, norm_before_gate=before)
+        torch.cuda.synchronize()
+        ref = oracle.gated_rmsnorm(wl.as_f64(yv, io), wl.as_f64(zv, io) if gate else None, w, eps, gs, before)
+        assert hp.rel_l2(hp.to_numpy64(out), ref) <= hp.TOL[io], f"norm {io} rows{rows} dim{dim} gs{gs}"
