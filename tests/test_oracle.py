@@ -10,6 +10,8 @@ import os
 
 import numpy as np
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 from oracle import oracle
 from selective_state_space_71_amd import workloads as wl
@@ -135,6 +137,21 @@ def test_quadratic_masked_form(G):
     yq = _quadratic(x, dt, A, B, C, D, h0)
     rel = np.linalg.norm(y - yq) / np.linalg.norm(yq)
     assert rel <= 1e-12
+
+
+@settings(max_examples=40, deadline=None)
+@given(b=st.integers(1, 2), L=st.integers(1, 20), Gi=st.integers(0, 1), hpg=st.integers(1, 2),
+       P=st.integers(1, 4), N=st.integers(1, 4), init=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_quadratic_masked_form_property(b, L, Gi, hpg, P, N, init, seed):
+    """The same pin over shapes drawn by hypothesis: any batch, length, group
+    count, heads per group, head and state dims, with or without an initial
+    state."""
+    G = Gi + 1
+    rng = np.random.default_rng(seed)
+    x, dt, A, B, C, D, h0 = _rand_case(rng, b=b, L=L, H=G * hpg, P=P, N=N, G=G, init=init)
+    y, _ = oracle.ssd_fwd(x, dt, A, B, C, D, init_state=h0)
+    yq = _quadratic(x, dt, A, B, C, D, h0)
+    assert np.max(np.abs(y - yq)) <= 1e-12 * max(1.0, np.max(np.abs(yq)))
 
 
 # ---------------------------------------------------------------- linear attention
