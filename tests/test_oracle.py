@@ -547,6 +547,31 @@ def test_backward_dA_term_scale():
     np.testing.assert_allclose(g2["dA_abs"], np.abs(terms).sum(axis=0), rtol=1e-6)
 
 
+@settings(max_examples=15, deadline=None)
+@given(L=st.integers(1, 6), Gi=st.integers(0, 1), P=st.integers(1, 3), N=st.integers(1, 3),
+       packed=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_backward_finite_differences_property(L, Gi, P, N, packed, seed):
+    """The finite-difference pin over hypothesis-drawn tiny shapes (one or
+    two groups of one head each, dense or split into two packed sequences)."""
+    G = Gi + 1
+    lengths = [L // 2, L - L // 2] if packed else None
+    p, cu, dy, dfin = _bwd_problem(seed, L=L, H=G, P=P, N=N, G=G, lengths=lengths)
+    g = oracle.ssd_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], dy, D=p["D"], init_state=p["init_state"],
+                       cu_seqlens=cu, dfinal=dfin)
+    eps = 1e-6
+    for k, gk in dict(x="dx", dt="ddt", A="dA", B="dB", C="dC", D="dD", init_state="dinit").items():
+        fd = np.zeros_like(p[k])
+        for idx in np.ndindex(p[k].shape):
+            keep = p[k][idx]
+            p[k][idx] = keep + eps
+            lp = _loss(p, cu, dy, dfin)
+            p[k][idx] = keep - eps
+            lm = _loss(p, cu, dy, dfin)
+            p[k][idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gk], fd, rtol=1e-6, atol=1e-7, err_msg=k)
+
+
 def test_backward_euler_identities():
     """y and final_state are jointly linear in (x, init) and linear in B and in
     C, so the gradient contracted with the input returns the loss exactly."""
