@@ -415,6 +415,21 @@ def test_causal_conv1d_matches_numpy_convolve():
         np.testing.assert_allclose(out[0, :, c], np.convolve(x[0, :, c], w[c, ::-1])[:40], rtol=0, atol=1e-13)
 
 
+@settings(max_examples=40, deadline=None)
+@given(b=st.integers(1, 3), L=st.integers(1, 50), Cc=st.integers(1, 6), W=st.integers(1, 4),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_causal_conv1d_numpy_convolve_property(b, L, Cc, W, seed):
+    """The numpy.convolve pin over hypothesis-drawn batches, lengths (shorter
+    than the taps included), channel counts and widths."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(b, L, Cc))
+    w = rng.normal(size=(Cc, W))
+    out, _ = oracle.causal_conv1d(x, w)
+    for bb in range(b):
+        for c in range(Cc):
+            np.testing.assert_allclose(out[bb, :, c], np.convolve(x[bb, :, c], w[c, ::-1])[:L], rtol=0, atol=1e-12)
+
+
 def test_causal_conv1d_varlen_split_and_state():
     rng = np.random.default_rng(23)
     W, Cc = 4, 6
