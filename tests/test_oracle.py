@@ -458,6 +458,27 @@ def test_causal_conv1d_varlen_split_and_state():
     np.testing.assert_array_equal(f2, fw)
 
 
+@settings(max_examples=40, deadline=None)
+@given(rows=st.integers(1, 5), ngr=st.integers(1, 4), gs=st.integers(1, 12), gate=st.booleans(),
+       before=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_gated_rmsnorm_group_and_scale_property(rows, ngr, gs, gate, before, seed):
+    """Over hypothesis-drawn shapes, with eps = 0: scaling y alone by a
+    positive factor leaves the output unchanged, whether the gate is applied
+    inside the norm (the normalized y silu(z) scales with y) or after it; and
+    every channel group equals the one-group norm of that slice on its own."""
+    rng = np.random.default_rng(seed)
+    dim = ngr * gs
+    y = rng.normal(size=(rows, dim))
+    z = rng.normal(size=(rows, dim)) if gate else None
+    w = rng.normal(size=dim)
+    out = oracle.gated_rmsnorm(y, z, w, 0.0, gs, before)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(3.7 * y, z, w, 0.0, gs, before), out, rtol=1e-12, atol=1e-12)
+    for k in range(ngr):
+        sl = slice(k * gs, (k + 1) * gs)
+        one = oracle.gated_rmsnorm(y[:, sl], None if z is None else z[:, sl], w[sl], 0.0, gs, before)
+        np.testing.assert_allclose(out[:, sl], one, rtol=1e-12, atol=1e-12)
+
+
 def test_gated_rmsnorm_pins():
     n34 = np.array([0.6, 0.8]) * math.sqrt(2.0)        # [3, 4] / rms([3, 4]), rms = 5 / sqrt(2)
     one = np.ones(2)
