@@ -62,10 +62,14 @@ typedef enum {
     SSD_ERR_ALIAS = 6,        /* an output overlaps an input it must not overlap     */
     SSD_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than the size query says  */
     SSD_ERR_HIP = 8,          /* the HIP runtime reported an error at launch         */
-    SSD_ERR_DEVICE = 9        /* a kernel reported an internal failure (see below)   */
+    SSD_ERR_DEVICE = 9,       /* a kernel reported an internal failure (see below)   */
+    SSD_STATUS_MAX_ENUM = 0x7fffffff  /* not a status: every value in [0, 2^31) is in range */
 } ssd_status_t;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;  /* dtype of x, B, C, y */
+/* dtype of x, B, C, y.  The last enumerator is not a dtype: it keeps every
+ * value in [0, 2^31) in the type's range, so an invalid value passed by a
+ * caller is rejected (SSD_ERR_DTYPE) rather than being undefined. */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_DTYPE_MAX_ENUM = 0x7fffffff } ssd_dtype_t;
 
 typedef struct {
     int32_t batch;    /* dense batch size; 1 for a packed varlen batch               */
