@@ -32,9 +32,11 @@
  *   - Arguments are validated synchronously before anything is launched; an
  *     invalid call returns a status and launches nothing.  No C++ exception
  *     crosses the ABI.
- *   - Preconditions that are documented but not checked: inputs are finite;
- *     cu_seqlens[0] == 0, cu_seqlens is non-decreasing and its last entry is
- *     seqlen.  Non-finite values stay inside their own sequence.
+ *   - Preconditions that are documented but not checked on the host: inputs
+ *     are finite; cu_seqlens[0] == 0, cu_seqlens is non-decreasing and its
+ *     last entry is seqlen.  Non-finite values stay inside their own sequence.
+ *     The forward's schedule kernel checks cu_seqlens on the device and, when
+ *     it is broken, processes nothing (ssd_chunk_scan_fwd_check reports it).
  *   - With the environment variable SSD_DEBUG_VALIDATE=1, every entry point
  *     that takes cu_seqlens copies it to the host first (this synchronises
  *     `stream`, so not under graph capture) and returns SSD_ERR_SHAPE,
@@ -179,10 +181,17 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Reads the device-side failure word of a workspace after a forward call
- * (synchronises `stream`).  Returns SSD_OK, or SSD_ERR_DEVICE when a chunk
- * waited too long for its predecessor's state (the outputs of that call are
- * then invalid), or SSD_ERR_HIP.  Meant for tests and diagnostics.
+ * Checks a forward call after the fact (synchronises `stream`, then reads the
+ * workspace header).  Returns
+ *   SSD_OK          the call ran to completion;
+ *   SSD_ERR_SHAPE   cu_seqlens broke its precondition (the kernel then
+ *                   processed no chunk: y and final_state were not written);
+ *   SSD_ERR_DEVICE  a chunk waited too long for its predecessor's state, or
+ *                   some accelerator complex (XCD) never drained its list of
+ *                   work items (every chain of chunks is bound to one XCD);
+ *                   the outputs of that call are then invalid;
+ *   SSD_ERR_HIP / SSD_ERR_WORKSPACE on a runtime error or a NULL workspace.
+ * Meant for tests and diagnostics; the forward call itself does not wait.
  */
 ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream);
 

@@ -39,6 +39,7 @@ struct PrepParams {
     const int *cu_seqlens;  // null for a dense batch
     int batch, seqlen, nseq, H, Q;
     int G, slices, n_xcd;
+    int max_entries;        // capacity of the chunk table
     int state_elems;        // P * N
     int4 *chunks;
     int *n_chunks;
@@ -54,21 +55,36 @@ struct PrepParams {
 };
 
 // Packed batch: chunk counts per sequence, their running sum, the
-// chunk-index-major table and the final state of empty sequences.
-__device__ void build_packed_schedule(const PrepParams &p) {
+// chunk-index-major table and the final state of empty sequences.  The
+// offsets are checked on the way (0 = cu[0] <= cu[1] <= ... <= cu[nseq] =
+// seqlen, and at most max_entries chunks): offsets that break this leave an
+// empty schedule (no chunk entries, so every forward workgroup exits at once
+// and nothing is read or written out of bounds) and set bit 1 of the error
+// word.  Returns false in that case.
+__device__ bool build_packed_schedule(const PrepParams &p) {
     const int tid = threadIdx.x;
     const int Q = p.Q;
+    __shared__ int s_valid;
     if (tid == 0) {
-        int acc = 0;
-        for (int s = 0; s < p.nseq; ++s) {
-            p.seq_chunk_start[s] = acc;
-            const int len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
-            acc += (len > 0) ? (len + Q - 1) / Q : 0;
+        long long acc = 0;
+        bool ok = p.cu_seqlens[0] == 0 && p.cu_seqlens[p.nseq] == p.seqlen;
+        for (int s = 0; s < p.nseq && ok; ++s) {
+            const int a = p.cu_seqlens[s], e = p.cu_seqlens[s + 1];
+            ok = a >= 0 && e >= a && e <= p.seqlen;
+            p.seq_chunk_start[s] = (int)acc;
+            acc += (e > a) ? (e - a + Q - 1) / Q : 0;
+            ok = ok && acc <= p.max_entries;
         }
-        p.seq_chunk_start[p.nseq] = acc;
-        *p.n_chunks = acc;
+        if (!ok) {
+            *p.error |= 2;
+            acc = 0;
+        }
+        p.seq_chunk_start[p.nseq] = (int)acc;
+        *p.n_chunks = (int)acc;
+        s_valid = ok ? 1 : 0;
     }
     __syncthreads();
+    if (!s_valid) return false;
     const int total = p.seq_chunk_start[p.nseq];
     for (int f = tid; f < total; f += 256) {
         int lo = 0, hi = p.nseq - 1;  // last s with seq_chunk_start[s] <= f
@@ -96,6 +112,7 @@ __device__ void build_packed_schedule(const PrepParams &p) {
                 p.final_state[base + k] = p.init_state ? p.init_state[base + k] : 0.f;
         }
     }
+    return true;
 }
 
 __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
@@ -121,7 +138,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
             p.chunks[e] = make_int4(s, c, s * p.seqlen + start, len);
         }
     } else {
-        build_packed_schedule(p);
+        build_packed_schedule(p);   // an invalid table leaves zero entries
     }
     __syncthreads();
     // per-XCD item lists: counts, offsets, then an order-preserving placement.
@@ -399,11 +416,13 @@ int num_compute_units() {
 }
 
 // Number of XCDs (accelerator complexes, each with its own L2) of the
-// current device, clamped to [1, 16].
+// current device, clamped to at most 16, or -1 when the runtime cannot tell.
+// The forward's hand-off keeps every chain on one XCD, so a wrong count is an
+// error, never silently replaced by a default.
 int num_xcds() {
     static std::atomic<int> cache[64] = {};
     const int n = device_attr(hipDeviceAttributeNumberOfXccs, cache);
-    return n < 1 ? 1 : (n > 16 ? 16 : n);
+    return n < 1 ? -1 : (n > 16 ? 16 : n);
 }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -621,7 +640,9 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
     const int slices = (int)((hpg + hs - 1) / hs);
     pp.G = d.ngroups;
     pp.slices = slices;
+    pp.max_entries = (int)w.max_entries;
     pp.n_xcd = num_xcds();
+    if (pp.n_xcd < 1) return SSD_ERR_HIP;
     hipLaunchKernelGGL(ssd::ssd_prep_kernel, dim3(1), dim3(256), 0, s, pp);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
 
@@ -660,13 +681,19 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
 
 ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream) {
     if (!workspace) return SSD_ERR_WORKSPACE;
-    int word = 0;
+    int32_t hdr[64] = {};   // the 256-byte workspace header
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipStreamSynchronize(s) != hipSuccess) return SSD_ERR_HIP;
-    if (hipMemcpy(&word, static_cast<const char *>(workspace) + kWsError, sizeof(int), hipMemcpyDeviceToHost) !=
-        hipSuccess)
-        return SSD_ERR_HIP;
-    return word ? SSD_ERR_DEVICE : SSD_OK;
+    if (hipMemcpy(hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost) != hipSuccess) return SSD_ERR_HIP;
+    const int32_t word = hdr[kWsError / 4];
+    if (word & 2) return SSD_ERR_SHAPE;
+    if (word) return SSD_ERR_DEVICE;
+    // every XCD's item list must have been drained: a workgroup takes tickets
+    // until one lies past its list, so the counter ends at or beyond the count
+    // exactly when every item of the list was taken (and so completed)
+    for (int x = 0; x < 16; ++x)
+        if (hdr[(kWsTickets / 4) + x] < hdr[(kWsXcdCount / 4) + x]) return SSD_ERR_DEVICE;
+    return SSD_OK;
 }
 
 ssd_status_t ssd_decode_step(const ssd_dims_t *dims, ssd_dtype_t io, float *state, const void *x,

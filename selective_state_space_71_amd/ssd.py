@@ -178,8 +178,15 @@ def workspace_size(dims: SsdDims, chunk_len: int, io: int) -> int:
 
 def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None,
                    cu_seqlens=None, return_final_state: bool = True, y=None, final_state=None,
-                   workspace=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None):
-    """SSD forward through ``ssd_chunk_scan_fwd_ex``.  Returns (y, final_state)."""
+                   workspace=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None,
+                   check: bool = False):
+    """SSD forward through ``ssd_chunk_scan_fwd_ex``.  Returns (y, final_state).
+
+    The call only enqueues the kernels.  Failures the device detects (a broken
+    ``cu_seqlens``, a chain wait that gave up, an XCD whose work list was not
+    drained) leave y and final_state invalid without an error here; with
+    ``check=True`` the binding synchronises and raises ``SsdError`` for them
+    (through ``ssd_chunk_scan_fwd_check``)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", device=dev)
@@ -228,6 +235,10 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None
     if code != 0:
         raise SsdError(code, "ssd_chunk_scan_fwd_ex")
     chunk_scan_fwd.last_workspace = workspace
+    if check:
+        code = lib.ssd_chunk_scan_fwd_check(_ptr(workspace), _stream(dev))
+        if code != 0:
+            raise SsdError(code, "ssd_chunk_scan_fwd_check")
     return y, final_state
 
 

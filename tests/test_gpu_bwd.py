@@ -178,6 +178,27 @@ def test_backward_full_size_sampled_heads():
         assert v <= 1e-2, (k, v)
 
 
+def test_backward_27b_shape_sampled_heads():
+    """The Mamba-2 2.7B-layer shape that bench.py times (batch 4, L 8192, 80
+    heads): every gradient on the GPU; dx, ddt, dinit, dA and dD of two
+    sampled heads against the oracle run on those heads only."""
+    inp = _inputs("bf16", 4, 8192, 80, 64, 128, 1, seed=103)
+    got = _gpu(inp)
+    heads = [5, 62]
+    mask = np.zeros((4, 80), dtype=bool)
+    mask[:, heads] = True
+    ref = _ref(inp, unit_mask=mask)
+    errs = {}
+    for k, axis in (("dx", 2), ("ddt", 2), ("dinit", 1)):
+        g = np.take(hp.to_numpy64(got[k]), heads, axis=axis)
+        errs[k] = hp.rel_l2(g, np.take(ref[k], heads, axis=axis))
+    for k in ("dA", "dD"):
+        errs[k] = hp.rel_l2(hp.to_numpy64(got[k])[heads], ref[k][heads])
+    print("[bwd 2.7B] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= 1e-2, (k, v)
+
+
 def test_backward_varlen_grouped_full_size_sampled_heads():
     """The packed variable-length workload (16 sequences, 65,536 tokens, 32
     heads in 8 groups, no initial state): every gradient on the GPU; the oracle

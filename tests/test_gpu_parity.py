@@ -409,11 +409,99 @@ def test_decode_steps_equal_forward():
 
 
 # ------------------------------------------------------------------ full workloads
+def _spans(inp):
+    """(batch row, first token, end) of every sequence."""
+    b, L = inp["x"].shape[:2]
+    cu = inp.get("cu_seqlens")
+    if cu is None:
+        return [(i, 0, L) for i in range(b)]
+    return [(0, int(cu[s]), int(cu[s + 1])) for s in range(len(cu) - 1)]
+
+
+def _chunk_sq(a, spans, Q):
+    """Squared L2 norm of a [b, L, H, P] array per (chunk, head): rows are the
+    chunks of every non-empty sequence in order, columns the heads."""
+    out = []
+    for bi, lo, hi in spans:
+        if hi > lo:
+            sq = np.einsum("thp,thp->th", a[bi, lo:hi], a[bi, lo:hi])
+            out.append(np.add.reduceat(sq, np.arange(0, hi - lo, Q), axis=0))
+    return np.concatenate(out)
+
+
+def _worst_unit_errors(inp, Q, y, y_ref, fin, fin_ref):
+    """Worst relative L2 over (sequence, head) units of y and the final state,
+    and over (chunk, head) units of y: a single wrong chunk or head cannot
+    hide in the whole-tensor figure."""
+    spans = _spans(inp)
+    err_c, ref_c = _chunk_sq(y - y_ref, spans, Q), _chunk_sq(y_ref, spans, Q)
+    seq_of_chunk = np.concatenate([np.full(-(-(hi - lo) // Q), s) for s, (_, lo, hi) in enumerate(spans)
+                                   if hi > lo])
+    nseq = len(spans)
+    err_u = np.zeros((nseq, err_c.shape[1]))
+    ref_u = np.zeros_like(err_u)
+    np.add.at(err_u, seq_of_chunk, err_c)
+    np.add.at(ref_u, seq_of_chunk, ref_c)
+    live_u = ref_u > 0
+    f_err = np.sqrt(((fin - fin_ref) ** 2).sum(axis=(2, 3)) / np.maximum((fin_ref ** 2).sum(axis=(2, 3)), 1e-300))
+    return dict(y_unit=float(np.sqrt(err_u[live_u] / ref_u[live_u]).max()),
+                y_chunk=float(np.sqrt(err_c[ref_c > 0] / ref_c[ref_c > 0]).max()),
+                final_unit=float(f_err.max()))
+
+
 @pytest.mark.parametrize("index", [1, 2, 3])
 def test_full_workload_forward(index):
     w = wl.WORKLOADS[index]
     print(f"[parity] full workload {w['name']}", flush=True)
-    _check_fwd(wl.workload_inputs(index), w["chunk"], tag=w["name"])
+    inp = wl.workload_inputs(index)
+    _check_fwd(inp, w["chunk"], tag=w["name"])
+    # the state-space part (D = 0) per (sequence, head) and per (chunk, head)
+    d = hp.to_device(inp, DEV)
+    y0, fin = _run(d, w["chunk"], D=False)
+    y_ref, fin_ref = hp.oracle_fwd(inp, D=False)
+    worst = _worst_unit_errors(inp, w["chunk"], hp.to_numpy64(y0), y_ref, hp.to_numpy64(fin), fin_ref)
+    print(f"[parity] {w['name']} worst " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()), flush=True)
+    for k, v in worst.items():
+        assert v <= hp.TOL[inp["io"]], (k, v)
+
+
+def test_check_reports_failures_from_the_header():
+    """ssd_chunk_scan_fwd_check reads the workspace header: an XCD whose ticket
+    counter ended below its item count (its list was not drained), the chain
+    timeout bit and the broken-offsets bit.  The headers are written from the
+    host; no kernel runs."""
+    ws = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    words = ws.view(torch.int32)           # tickets [0, 16), error 16, counts [32, 48)
+    words[32 + 3] = 5
+    words[3] = 5
+    assert ssd.check_workspace(ws) == 0
+    words[3] = 4
+    assert ssd.check_workspace(ws) == 9    # SSD_ERR_DEVICE
+    words[3] = 6
+    words[16] = 1
+    assert ssd.check_workspace(ws) == 9
+    words[16] = 2
+    assert ssd.check_workspace(ws) == 2    # SSD_ERR_SHAPE
+
+
+@pytest.mark.parametrize("cu", [[0, 200, 100, 300], [0, 100, 400]])
+def test_broken_cu_seqlens_processes_nothing(cu):
+    """Offsets that break the precondition (here decreasing, or ending past
+    the token count) are caught by the schedule kernel: no chunk is processed
+    and the check reports SSD_ERR_SHAPE.  The buffers are views into larger
+    allocations, and the chunk table holds every chunk these offsets would
+    make, so even an unchecked schedule would stay in bounds."""
+    T = 300
+    inp = wl.make_inputs(1, 2 * T, 2, 64, 64, 1, io="bf16", seed=43)
+    d = hp.to_device(inp, DEV)
+    y_big = torch.full_like(d["x"], 7.0)
+    view = lambda t: t[:, :T]
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    with pytest.raises(ssd.SsdError, match="SSD_ERR_SHAPE"):
+        ssd.chunk_scan_fwd(view(d["x"]), view(d["dt"]), d["A"], view(d["B"]), view(d["C"]), d["D"],
+                           chunk_len=64, cu_seqlens=cu_t, y=view(y_big), check=True)
+    torch.cuda.synchronize()
+    assert bool((y_big == 7.0).all())
 
 
 def test_full_workload_decode():
