@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum {
     SSD_OK = 0,
@@ -179,6 +179,32 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
                                    const float *init_state, const int32_t *cu_seqlens,
                                    void *y, float *final_state,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the device scratch array behind ssd_chunk_scan_fwd_noalloc. */
+#define SSD_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * ssd_chunk_scan_fwd_ex that allocates nothing and takes no workspace: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * semantics, outputs and status codes as ssd_chunk_scan_fwd_ex, minus the
+ * workspace.  The workspace it would need (ssd_chunk_scan_fwd_workspace_size,
+ * less the boundary-state part when final_state is given) lives in a
+ * library-owned device array of SSD_NOALLOC_SCRATCH_BYTES (32 MiB), one per
+ * device, held from the first call on that device until the process ends.
+ * Dimensions whose workspace exceeds it return SSD_ERR_WORKSPACE and launch
+ * nothing.  The schedule kernel clears what must start at zero on every call.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (different streams, different threads) race and give
+ * undefined results; serialise them.  There is no check call for this entry
+ * point (the failure word sits in the shared array).
+ */
+ssd_status_t ssd_chunk_scan_fwd_noalloc(const ssd_dims_t *dims, ssd_dtype_t io_dtype,
+                                        int32_t chunk_len, const ssd_dt_opts_t *dt_opts,
+                                        const void *x, const float *dt, const float *A,
+                                        const void *B, const void *C, const float *D,
+                                        const float *init_state, const int32_t *cu_seqlens,
+                                        void *y, float *final_state, void *stream);
 
 /*
  * Checks a forward call after the fact (synchronises `stream`, then reads the

@@ -380,6 +380,38 @@ static bool norm_launch(int nch, int mode, const NormParams &p, unsigned blocks,
 // C ABI
 namespace {
 
+// Scratch of ssd_chunk_scan_fwd_noalloc: the workspace of one call (header,
+// progress flags, chunk table, item lists and, when the caller passes no
+// final_state, the boundary states), in a file-scope device array so that
+// the call allocates nothing.  Each device holds its own copy for the life
+// of the process; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = SSD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// This device's address of `scratch`, looked up on the first call on each
+// device (with that device current) and cached; SSD_ERR_HIP if the runtime
+// cannot resolve it.  Concurrent first calls store the same address.
+ssd_status_t scratch_base(char **out) {
+    static std::atomic<char *> cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    const bool cached = dev >= 0 && dev < 64;
+    if (cached) {
+        char *c = cache[dev].load(std::memory_order_acquire);
+        if (c) {
+            *out = c;
+            return SSD_OK;
+        }
+    }
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SSD_ERR_HIP;
+    if (cached) cache[dev].store(static_cast<char *>(ptr), std::memory_order_release);
+    *out = static_cast<char *>(ptr);
+    return SSD_OK;
+}
+
 struct Range {
     uintptr_t lo, hi;
 };
@@ -556,12 +588,17 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32_t 
                                  final_state, workspace, workspace_bytes, stream);
 }
 
-ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
-                                   const ssd_dt_opts_t *dt_opts, const void *x, const float *dt,
-                                   const float *A, const void *B, const void *C, const float *D,
-                                   const float *init_state, const int32_t *cu_seqlens, void *y,
-                                   float *final_state, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
+}  // extern "C"
+
+namespace {
+// The forward entry points.  `scratch_mode` runs the call on this device's
+// copy of the file-scope scratch array instead of a caller workspace
+// (`workspace` and `workspace_bytes` are then ignored).
+ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len, const ssd_dt_opts_t *dt_opts,
+                      const void *x, const float *dt, const float *A, const void *B, const void *C,
+                      const float *D, const float *init_state, const int32_t *cu_seqlens, void *y,
+                      float *final_state, void *workspace, size_t workspace_bytes, bool scratch_mode,
+                      void *stream) {
     const bool varlen = cu_seqlens != nullptr;
     ssd_status_t st = fwd_shape_check(dims, chunk_len, io, varlen);
     if (st != SSD_OK) return st;
@@ -570,11 +607,11 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
     if (st != SSD_OK) return st;
     const ssd_dims_t &d = *dims;
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_PTR;
-    if (!workspace) return SSD_ERR_WORKSPACE;
+    if (!scratch_mode && !workspace) return SSD_ERR_WORKSPACE;
     const void *al16[] = {x, dt, A, B, C, D, init_state, y, final_state, dtp.bias};
     for (const void *p : al16)
         if (p && !aligned(p, 16)) return SSD_ERR_ALIGNMENT;
-    if (!aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
+    if (!scratch_mode && !aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
 
     const size_t E = (io == SSD_BF16) ? 2 : 4;
@@ -591,8 +628,15 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
     if (overlap(ry, rbias) || overlap(rf, rbias)) return SSD_ERR_ALIAS;
     WsLayout w{};
     ws_layout(d, chunk_len, varlen, &w);
-    if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
-    const Range rw = rng(workspace, w.total);
+    if (scratch_mode) {
+        // the boundary-state part is needed only when final_state is NULL
+        if ((final_state ? w.state : w.total) > kNoAllocScratchBytes) return SSD_ERR_WORKSPACE;
+    } else if (workspace_bytes < w.total) {
+        return SSD_ERR_WORKSPACE;
+    }
+    // (the scratch array is the library's own memory: no caller buffer can
+    // overlap it, so these checks pass in scratch mode)
+    const Range rw = rng(workspace, scratch_mode ? 0 : w.total);
     for (Range r : {rx, rdt, rA, rB, rC, rD, ri, rf, rcu, rw})
         if (overlap(ry, r)) return SSD_ERR_ALIAS;
     for (Range r : {rx, rdt, rA, rB, rC, rD, rcu, rw})
@@ -601,6 +645,12 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
     for (Range r : {rx, rdt, rA, rB, rC, rD, ri, rcu})
         if (overlap(rw, r)) return SSD_ERR_ALIAS;
     if (w.max_entries * d.nheads > INT_MAX) return SSD_ERR_SHAPE;
+    if (scratch_mode) {
+        char *base = nullptr;
+        const ssd_status_t sst = scratch_base(&base);
+        if (sst != SSD_OK) return sst;
+        workspace = base;
+    }
 
     char *ws = static_cast<char *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -677,6 +727,28 @@ ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32
     if (!ok) return SSD_ERR_UNSUPPORTED;
     if (err != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
+}
+}  // namespace
+
+extern "C" {
+
+ssd_status_t ssd_chunk_scan_fwd_ex(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
+                                   const ssd_dt_opts_t *dt_opts, const void *x, const float *dt,
+                                   const float *A, const void *B, const void *C, const float *D,
+                                   const float *init_state, const int32_t *cu_seqlens, void *y,
+                                   float *final_state, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    return fwd_impl(dims, io, chunk_len, dt_opts, x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state,
+                    workspace, workspace_bytes, false, stream);
+}
+
+ssd_status_t ssd_chunk_scan_fwd_noalloc(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
+                                        const ssd_dt_opts_t *dt_opts, const void *x, const float *dt,
+                                        const float *A, const void *B, const void *C, const float *D,
+                                        const float *init_state, const int32_t *cu_seqlens, void *y,
+                                        float *final_state, void *stream) {
+    return fwd_impl(dims, io, chunk_len, dt_opts, x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state,
+                    nullptr, 0, true, stream);
 }
 
 ssd_status_t ssd_chunk_scan_fwd_check(const void *workspace, void *stream) {

@@ -87,6 +87,11 @@ def load_library(path: str = LIB_PATH):
         _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
         _VP, ctypes.c_size_t, _VP,
     ]
+    lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [
+        ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.c_int32, ctypes.POINTER(SsdDtOpts),
+        _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+    ]
     lib.ssd_decode_step_ex.restype = ctypes.c_int
     lib.ssd_decode_step_ex.argtypes = [
         ctypes.POINTER(SsdDims), ctypes.c_int, ctypes.POINTER(SsdDtOpts),
@@ -239,6 +244,49 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None
         code = lib.ssd_chunk_scan_fwd_check(_ptr(workspace), _stream(dev))
         if code != 0:
             raise SsdError(code, "ssd_chunk_scan_fwd_check")
+    return y, final_state
+
+
+def chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, chunk_len: int = 256, init_state=None,
+                           cu_seqlens=None, y=None, final_state=None, dt_bias=None,
+                           dt_softplus: bool = False, dt_limit=None):
+    """SSD forward through ``ssd_chunk_scan_fwd_noalloc``: no workspace; the
+    library's per-device scratch array holds the schedule (and the boundary
+    states when ``final_state`` is None).  Returns (y, final_state or None).
+    With ``y`` (and ``final_state``) passed in, nothing is allocated here
+    either.  Calls that overlap in time on one device race (they share the
+    scratch array)."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    io = _io_code(x)
+    b, L, H, P = x.shape
+    if B.dim() != 4 or B.shape[:2] != (b, L):
+        raise ValueError("B must be [batch, seqlen, ngroups, dstate]")
+    G, N = B.shape[2], B.shape[3]
+    _need(dt, "dt", torch.float32, (b, L, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(B, "B", x.dtype, (b, L, G, N), dev)
+    _need(C, "C", x.dtype, (b, L, G, N), dev)
+    if D is not None:
+        _need(D, "D", torch.float32, (H,), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    dims = fwd_dims(x, B, cu_seqlens)
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (dims.nseq, H, P, N), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, x.shape, dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (dims.nseq, H, P, N), dev)
+    opts = _dt_opts(dt_bias, dt_softplus, dt_limit, H, dev)
+    code = lib.ssd_chunk_scan_fwd_noalloc(
+        ctypes.byref(dims), io, int(chunk_len), None if opts is None else ctypes.byref(opts),
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+        _ptr(cu_seqlens), _ptr(y), _ptr(final_state), _stream(dev))
+    if code != 0:
+        raise SsdError(code, "ssd_chunk_scan_fwd_noalloc")
     return y, final_state
 
 

@@ -25,7 +25,8 @@ def test_header_symbols_are_exported(lib):
     assert {"ssd_chunk_scan_fwd", "ssd_decode_step", "ssd_chunk_scan_fwd_workspace_size",
             "ssd_status_string", "ssd_abi_version", "ssd_chunk_scan_fwd_check",
             "ssd_chunk_scan_fwd_ex", "ssd_decode_step_ex", "ssd_causal_conv1d_fwd",
-            "ssd_gated_rmsnorm_fwd", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size"} <= set(names)
+            "ssd_gated_rmsnorm_fwd", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
+            "ssd_chunk_scan_fwd_noalloc"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -35,7 +36,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 4
+    assert lib.ssd_abi_version() == 5
     for code, name in ssd._STATUS.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(77)
@@ -268,6 +269,34 @@ def test_bwd_validation_rejects(lib, case, expect):
     assert _bwd(lib, dims, **case) == expect
 
 
+def _fwd_noalloc(lib, dims, io=ssd.SSD_BF16, Q=256, **ptrs):
+    dp = dict(x=FAKE, dt=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+              C=FAKE + (4 << 30), D=None, init=None, cu=None, y=FAKE + (8 << 30), fin=None)
+    dp.update(ptrs)
+    return lib.ssd_chunk_scan_fwd_noalloc(
+        ctypes.byref(dims) if dims is not None else None, io, Q, None, dp["x"], dp["dt"], dp["A"],
+        dp["B"], dp["C"], dp["D"], dp["init"], dp["cu"], dp["y"], dp["fin"], None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), 1),
+    (dict(io=5), 3),
+    (dict(Q=100), 4),
+    (dict(dims=_dims(headdim=48)), 4),
+    (dict(x=None), 1),
+    (dict(x=FAKE + 2), 5),
+    (dict(y=FAKE + 64), 6),
+    # 16 sequences x 80 heads of 64 x 128 fp32 boundary states (42 MB) do not
+    # fit the 32 MiB scratch when final_state is NULL
+    (dict(dims=_dims(batch=16, nseq=16, seqlen=1024, nheads=80)), 7),
+])
+def test_noalloc_forward_validation_rejects(lib, case, expect):
+    """The allocation-free forward validates like the workspace one and
+    rejects schedules beyond its scratch array before touching the device."""
+    dims = case.pop("dims", _dims())
+    assert _fwd_noalloc(lib, dims, **case) == expect
+
+
 # (last: it reloads the binding module, which redefines its ctypes structures)
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
@@ -278,3 +307,4 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         importlib.reload(ssd)
+
