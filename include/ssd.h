@@ -153,10 +153,14 @@ size_t ssd_chunk_scan_fwd_workspace_size(const ssd_dims_t *dims, int32_t chunk_l
  *   stream      hipStream_t, or NULL for the default stream.
  *
  * Supported sizes: headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
- * 256}; chunk_len in {64, 128, 256}; combinations whose chunk tiles do not
- * fit in the 160 KB of LDS of a gfx950 compute unit return
- * SSD_ERR_UNSUPPORTED (bf16: headdim 128 or dstate 256 need chunk_len <= 128,
- * both together chunk_len 64; fp32 io needs smaller chunks still).
+ * 256}; chunk_len in {64, 128, 256}, every combination, both io dtypes.
+ * Head dim 128 runs as two 64-channel halves (each state row depends only on
+ * its own channel).  Where the tiles of chunk_len tokens do not fit in the
+ * 160 KB of LDS of a gfx950 compute unit (bf16: dstate 256 with chunk_len
+ * 256 and headdim >= 32; fp32: headdim >= 64 with chunk_len 256, and some
+ * larger shapes at 128), the kernel runs the largest shorter chunk that fits
+ * (at least 64 tokens): chunking only orders the evaluation, so the result is
+ * the same up to rounding.  Other sizes return SSD_ERR_UNSUPPORTED.
  * x, y, B, C, dt, D and the states must be 16-byte aligned.
  */
 ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,

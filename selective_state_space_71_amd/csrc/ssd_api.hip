@@ -478,6 +478,19 @@ ssd_status_t debug_check_cu_seqlens(const int32_t *cu, int nseq, int seqlen, hip
     return SSD_OK;
 }
 
+// The forward kernel's view of the heads: head dim 128 runs as two kernel
+// heads of 64 channels each (x, y and the states then have exactly the layout
+// of twice the heads at half the head dim; the kernel indexes dt, A, D and
+// dt_bias by the model head).
+struct KHeads {
+    int H, P, hsub;
+};
+
+KHeads kernel_heads(const ssd_dims_t &d) {
+    const int hsub = d.headdim == 128 ? 2 : 1;
+    return KHeads{d.nheads * hsub, d.headdim / hsub, hsub};
+}
+
 struct WsLayout {
     size_t flags, chunks, items, scratch, state, total;
     long long max_entries;
@@ -492,11 +505,12 @@ constexpr size_t kWsTickets = 0, kWsError = 64, kWsEntries = 68, kWsXcdCount = 1
 // boundary-state buffer.
 bool ws_layout(const ssd_dims_t &d, int Q, bool varlen, WsLayout *w) {
     const long long nc = ((long long)d.seqlen + Q - 1) / Q;
+    const int kh = kernel_heads(d).H;
     w->max_entries = varlen ? nc + d.nseq : nc * d.batch;
     w->flags = 256;
-    w->chunks = align_up(w->flags + (size_t)d.nseq * d.nheads * 4, 256);
+    w->chunks = align_up(w->flags + (size_t)d.nseq * kh * 4, 256);
     w->items = align_up(w->chunks + (size_t)w->max_entries * 16, 256);
-    w->scratch = align_up(w->items + (size_t)w->max_entries * d.nheads * 4, 256);
+    w->scratch = align_up(w->items + (size_t)w->max_entries * kh * 4, 256);
     w->state = align_up(w->scratch + (size_t)(d.nseq + 1) * 4, 256);
     w->total = align_up(w->state + (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4, 256);
     return true;
@@ -521,6 +535,22 @@ ssd_status_t dt_opts_check(const ssd_dt_opts_t *o, const ssd_dims_t &d, ssd::DtP
     return SSD_OK;
 }
 
+// The chunk length the kernel runs for a requested chunk_len: chunk_len
+// itself where its tiles fit in LDS, else the largest smaller one (at least
+// 64) that fits, or 0 when none is built.  Chunking only orders the
+// evaluation (the result is the recurrence's either way, up to rounding).
+int kernel_chunk(const ssd_dims_t &d, int32_t chunk_len, ssd_dtype_t io) {
+    ssd::FwdParams dummy{};
+    hipError_t e = hipSuccess;
+    for (int q = chunk_len; q >= 64; q /= 2) {
+        const bool built = (io == SSD_BF16)
+                               ? ssd::fwd_dispatch_bf16(kernel_heads(d).P, d.dstate, q, dummy, 0, nullptr, false, &e)
+                               : ssd::fwd_dispatch_f32(kernel_heads(d).P, d.dstate, q, dummy, 0, nullptr, false, &e);
+        if (built) return q;
+    }
+    return 0;
+}
+
 ssd_status_t fwd_shape_check(const ssd_dims_t *dims, int32_t chunk_len, ssd_dtype_t io, bool varlen) {
     if (!dims) return SSD_ERR_NULL_PTR;
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
@@ -532,12 +562,7 @@ ssd_status_t fwd_shape_check(const ssd_dims_t *dims, int32_t chunk_len, ssd_dtyp
         return SSD_ERR_SHAPE;
     }
     if (chunk_len != 64 && chunk_len != 128 && chunk_len != 256) return SSD_ERR_UNSUPPORTED;
-    ssd::FwdParams dummy{};
-    hipError_t e = hipSuccess;
-    const bool built = (io == SSD_BF16)
-                           ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, dummy, 0, nullptr, false, &e)
-                           : ssd::fwd_dispatch_f32(d.headdim, d.dstate, chunk_len, dummy, 0, nullptr, false, &e);
-    if (!built) return SSD_ERR_UNSUPPORTED;
+    if (kernel_chunk(d, chunk_len, io) == 0) return SSD_ERR_UNSUPPORTED;
     // sizes must stay within the kernels' 32-bit schedule fields
     const long long tokens = (long long)d.batch * d.seqlen;
     if (tokens > INT_MAX / 2) return SSD_ERR_SHAPE;
@@ -574,8 +599,9 @@ size_t ssd_chunk_scan_fwd_workspace_size(const ssd_dims_t *dims, int32_t chunk_l
         fwd_shape_check(dims, chunk_len, io, false) != SSD_OK)
         return 0;
     WsLayout packed{}, dense{};
-    ws_layout(*dims, chunk_len, true, &packed);
-    ws_layout(*dims, chunk_len, false, &dense);
+    const int q = kernel_chunk(*dims, chunk_len, io);
+    ws_layout(*dims, q, true, &packed);
+    ws_layout(*dims, q, false, &dense);
     return packed.total > dense.total ? packed.total : dense.total;
 }
 
@@ -602,6 +628,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     const bool varlen = cu_seqlens != nullptr;
     ssd_status_t st = fwd_shape_check(dims, chunk_len, io, varlen);
     if (st != SSD_OK) return st;
+    chunk_len = kernel_chunk(*dims, chunk_len, io);
     ssd::DtProc dtp{};
     st = dt_opts_check(dt_opts, *dims, &dtp);
     if (st != SSD_OK) return st;
@@ -644,7 +671,8 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     if (final_state && init_state && overlap(rf, ri) && rf.lo != ri.lo) return SSD_ERR_ALIAS;
     for (Range r : {rx, rdt, rA, rB, rC, rD, ri, rcu})
         if (overlap(rw, r)) return SSD_ERR_ALIAS;
-    if (w.max_entries * d.nheads > INT_MAX) return SSD_ERR_SHAPE;
+    const KHeads kh = kernel_heads(d);
+    if (w.max_entries * kh.H > INT_MAX || (long long)d.nseq * kh.H > INT_MAX) return SSD_ERR_SHAPE;
     if (scratch_mode) {
         char *base = nullptr;
         const ssd_status_t sst = scratch_base(&base);
@@ -661,9 +689,9 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     pp.batch = d.batch;
     pp.seqlen = d.seqlen;
     pp.nseq = d.nseq;
-    pp.H = d.nheads;
+    pp.H = kh.H;
     pp.Q = chunk_len;
-    pp.state_elems = d.headdim * d.dstate;
+    pp.state_elems = kh.P * d.dstate;
     pp.chunks = reinterpret_cast<int4 *>(ws + w.chunks);
     pp.n_chunks = reinterpret_cast<int *>(ws + kWsEntries);
     pp.tickets = reinterpret_cast<int *>(ws + kWsTickets);
@@ -680,9 +708,9 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     // the workgroups sharing an XCD walk many different heads at a time
     const int cus = num_compute_units();
     if (cus <= 0) return SSD_ERR_HIP;
-    const int hpg = d.nheads / d.ngroups;
+    const int hpg = kh.H / d.ngroups;
     const long long want = 8LL * cus;
-    long long hs = (w.max_entries * d.nheads + want - 1) / want;
+    long long hs = (w.max_entries * kh.H + want - 1) / want;
     hs = hs < 1 ? 1 : (hs > hpg ? hpg : hs);
     // but at least two heads where the group has them: an item's set-up (its
     // B chunk into LDS, the C B^T tiles) costs about as much as one head
@@ -716,14 +744,15 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     fp.n_xcd = pp.n_xcd;
     fp.flags = pp.flags;
     fp.error = pp.error;
-    fp.H = d.nheads;
+    fp.H = kh.H;
+    fp.hsub = kh.hsub;
     fp.G = d.ngroups;
     fp.heads_per_item = (int)hs;
     fp.slices = slices;
     hipError_t err = hipSuccess;
     const bool ok = (io == SSD_BF16)
-                        ? ssd::fwd_dispatch_bf16(d.headdim, d.dstate, chunk_len, fp, w.max_entries, s, true, &err)
-                        : ssd::fwd_dispatch_f32(d.headdim, d.dstate, chunk_len, fp, w.max_entries, s, true, &err);
+                        ? ssd::fwd_dispatch_bf16(kh.P, d.dstate, chunk_len, fp, w.max_entries, s, true, &err)
+                        : ssd::fwd_dispatch_f32(kh.P, d.dstate, chunk_len, fp, w.max_entries, s, true, &err);
     if (!ok) return SSD_ERR_UNSUPPORTED;
     if (err != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;

@@ -40,7 +40,6 @@
 namespace ssd {
 
 constexpr int kBwdQ = 64;         // tokens per chunk of the backward pass
-constexpr float kBwdLog2e = 1.4426950408889634f;
 
 struct BwdParams {
     const void *x, *B, *C, *dy;   // io
@@ -85,40 +84,11 @@ __device__ __forceinline__ f32x4 mma_tile(f32x4 acc, int K, int lg, FA fa, FB fb
 template <typename IO> __device__ __forceinline__ float split_hi(float v) { return to_f32(from_f32<IO>(v)); }
 template <typename IO> __device__ __forceinline__ float split_lo(float v) { return v - split_hi<IO>(v); }
 
-// v + (v of the lane the DPP control `ctrl` selects); lanes without a source
-// (or outside `row_mask`) add 0.
-template <int ctrl, int row_mask>
-__device__ __forceinline__ float bwd_dpp_add(float v) {
-    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask, 0xF, true);
-    return v + __builtin_bit_cast(float, t);
-}
-
-// Sum over the 16 lanes of each row of the wave, in every lane of the row:
-// pairs, quads, then the mirrored half and the mirrored row.
-__device__ __forceinline__ float bwd_row_sum(float v) {
-    v = bwd_dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-    v = bwd_dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-    v = bwd_dpp_add<0x141, 0xF>(v);   // row_half_mirror
-    v = bwd_dpp_add<0x140, 0xF>(v);   // row_mirror
-    return v;
-}
-
 // Sum over the 64 lanes (wave-uniform result), in a fixed order.
 __device__ __forceinline__ float bwd_wave_sum(float v) {
-    v = bwd_row_sum(v);
+    v = row_sum16(v);
     const auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
     return (rl(0) + rl(16)) + (rl(32) + rl(48));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float bwd_wave_scan(float v, int) {
-    v = bwd_dpp_add<0x111, 0xF>(v);   // row_shr:1
-    v = bwd_dpp_add<0x112, 0xF>(v);   // row_shr:2
-    v = bwd_dpp_add<0x114, 0xF>(v);   // row_shr:4
-    v = bwd_dpp_add<0x118, 0xF>(v);   // row_shr:8
-    v = bwd_dpp_add<0x142, 0xA>(v);   // row_bcast:15
-    v = bwd_dpp_add<0x143, 0xC>(v);   // row_bcast:31
-    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -239,7 +209,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_kernel(BwdParams p) {
         stage_rows<IO, N>(sv, vg, t0, q, (long long)p.G * N, (long long)g * N, tid);
         if (wave == 0) {
             const float d = lane < q ? p.dt[(t0 + lane) * p.H + h] : 0.f;
-            const float sc = bwd_wave_scan(d * Ah, lane) * kBwdLog2e;   // s * log2(e)
+            const float sc = wave_inclusive_sum(d * Ah) * kLog2e;   // s * log2(e)
             const float slast = __shfl(sc, 63, 64);
             swt[lane] = MODE == 0 ? __builtin_amdgcn_exp2f(slast - sc) * d : __builtin_amdgcn_exp2f(sc);
             if (lane == 0) salpha = __builtin_amdgcn_exp2f(slast);
@@ -338,7 +308,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
         const float Ah = p.A[h];
         if (wave == 0) {
             const float d = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
-            const float sc = bwd_wave_scan(d * Ah, lane) * kBwdLog2e;
+            const float sc = wave_inclusive_sum(d * Ah) * kLog2e;
             const float slast = __shfl(sc, 63, 64);
             s2[lane] = sc;
             dtv[lane] = d;
@@ -481,7 +451,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
             const float rh = __builtin_amdgcn_exp2f(s2[Q - 1]) * hrd + bwd_wave_sum(d * offB[j]);
             float ds = rowZ[j] - d * colZ[j] + offC[j] - d * offB[j] + (j == q - 1 ? rh : 0.f);
             const float tot = bwd_wave_sum(ds);
-            const float da = tot - bwd_wave_scan(ds, lane) + ds;    // sum over i >= j
+            const float da = tot - wave_inclusive_sum(ds) + ds;    // sum over i >= j
             if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + colZ[j] + offB[j];
             const float pa = bwd_wave_sum(d * da);
             if (lane == 0) p.partA[(long long)ci * H + h] = pa;
@@ -685,7 +655,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         if (lane == 0) hrp[wave] = hrd;
         const float Ah = p.A[h];
         if (wave == 0) {
-            const float sc = bwd_wave_scan(dtr * Ah, lane) * kBwdLog2e;
+            const float sc = wave_inclusive_sum(dtr * Ah) * kLog2e;
             const float slast = __shfl(sc, 63, 64);
             s2[lane] = sc;
             dtv[lane] = dtr;
@@ -728,7 +698,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                rz[r] = bwd_row_sum(rz[r]);
+                rz[r] = row_sum16(rz[r]);
                 if (li == 0) rowP[half][row0 + 4 * lg + r] = rz[r];
             }
         }
@@ -797,8 +767,8 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            ob[r] = bwd_row_sum(ob[r]);
-            oc[r] = bwd_row_sum(oc[r]);
+            ob[r] = row_sum16(ob[r]);
+            oc[r] = row_sum16(oc[r]);
             if (li == 0) {
                 offBP[half][row0 + 4 * lg + r] = ob[r];
                 offCP[half][row0 + 4 * lg + r] = oc[r];
@@ -824,7 +794,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             const float rh = __builtin_amdgcn_exp2f(s2[Q - 1]) * hrs + bwd_wave_sum(d * ob_);
             const float ds = rz - d * cz + oc_ - d * ob_ + (j == q - 1 ? rh : 0.f);
             const float tot = bwd_wave_sum(ds);
-            const float da = tot - bwd_wave_scan(ds, lane) + ds;
+            const float da = tot - wave_inclusive_sum(ds) + ds;
             if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + cz + ob_;
             const float pa = bwd_wave_sum(d * da);
             if (lane == 0) p.partA[(long long)ci * H + h] = pa;
@@ -967,7 +937,7 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
             *reinterpret_cast<bf16x8 *>(sv + j * SN + c8) = vr[k];
         }
         if (wave == 0) {
-            const float sc = bwd_wave_scan(dtr * Ah, lane) * kBwdLog2e;
+            const float sc = wave_inclusive_sum(dtr * Ah) * kLog2e;
             const float slast = __shfl(sc, 63, 64);
             swt[lane] = mode == 0 ? __builtin_amdgcn_exp2f(slast - sc) * dtr : __builtin_amdgcn_exp2f(sc);
             if (lane == 0) salpha = __builtin_amdgcn_exp2f(slast);

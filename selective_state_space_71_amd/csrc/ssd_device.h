@@ -71,6 +71,41 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16 *p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2f_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// v + (v of the lane the DPP control `ctrl` selects); lanes without a source
+// (or outside `row_mask`) add 0.
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask, 0xF, true);
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: four
+// shifts inside each 16-lane row, then the last lane of rows 0 and 2 into
+// rows 1 and 3, then lane 31 into rows 2 and 3.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+    v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+    v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+    v = dpp_add<0x118, 0xF>(v);   // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31
+    return v;
+}
+
+// Sum over the 16 lanes of each row of the wave, in every lane of the row:
+// pairs, quads, then the mirrored half and the mirrored row.
+__device__ __forceinline__ float row_sum16(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror
+    return v;
+}
+
 // Step-size preprocessing (see ssd_dt_opts_t): dt = clamp(softplus(dt + bias)).
 struct DtProc {
     const float *bias;   // [nheads] or null

@@ -12,14 +12,33 @@
 //   Y_off   = diag(exp(s_i)) C H_c^T
 //   y       = Y_diag + Y_off + D_h x
 //
+// Decay by blocks.  The chunk is cut into blocks of 64 tokens; e_b is the
+// cumulative sum at the last token of block b.  Each head's x is staged twice
+// in LDS: as is, and as
+//   xh_j = exp(e_b(j) - s_j) dt_j x_j            (a factor <= 1 per token).
+// For a row i in block R and a column j in an earlier block b < R,
+//   exp(s_i - s_j) = exp(s_i - e_{R-1}) * exp(e_{R-1} - e_b) * exp(e_b - s_j),
+// every factor <= 1 (A <= 0, dt >= 0), so the part of Y_diag that lies left of
+// the row's own block is
+//   diag(exp(s_i - e_{R-1})) sum_{b<R} exp(e_{R-1} - e_b) G[i, block b] xh_b,
+// a sum that is accumulated block by block (Horner's rule: scale the
+// accumulator by the block decay exp(e_b - e_{b-1}), then add block b's
+// product).  Those products take the C B^T tiles straight from registers as
+// MFMA operands: no per-element work.  Only the row's own 64-token block is
+// built explicitly (decay-weighted mask, with a per-element exponential on the
+// diagonal 16 x 16 tiles and row x column factors on the others).  The chunk
+// state uses the same staged xh with the same recurrence over all blocks:
+//   S_c = sum_b exp(e_last - e_b) B_b^T xh_b.
+//
 // Work decomposition.  A workgroup (8 waves) owns one chunk of one B/C group
 // and a slice of that group's heads.  C B^T depends only on the chunk and the
 // group (heads of a group share B and C: the multi-input head pattern of
 // section 3-2(5)), so it is formed once per workgroup and kept in registers:
 // wave w owns the 16-row tiles w and 15 - w of the chunk (balanced causal
-// work) and holds their lower-triangular C B^T tiles.  B stays in LDS and the
-// wave's C rows stay in registers while the workgroup walks over its heads;
-// per head only x and dt are loaded (prefetched during the previous head).
+// work) and holds their lower-triangular C B^T tiles.  The B^T operands of the
+// chunk state (the wave's state columns over the whole chunk) are also
+// head-independent and stay in registers where they fit.  Per head only x and
+// dt are loaded (prefetched during the previous head).
 //
 // Chain.  Work items (chunk entry, group, head slice) are listed per XCD:
 // all chunks of one (sequence, group, slice) chain belong to the same XCD, and
@@ -35,13 +54,8 @@
 // is the caller's final_state (or workspace); it ends up holding the final
 // state.
 //
-// Numerics.  All decays are products of factors <= 1 (A <= 0, dt >= 0):
-// for a 16 x 16 tile (I, J) below the diagonal,
-//   exp(s_i - s_j) = exp(s_i - s_r) * exp(s_r - s_j),  r = last token of tile J,
-// so only the diagonal tiles need a per-element exponential; the chunk-state
-// weights exp(s_{q-1} - s_j) and the read-out weights exp(s_i) are per-token
-// vectors.  Exponentials are evaluated as exp2 of log2(e)-scaled sums.
-// Accumulation and the boundary state are fp32.
+// Exponentials are evaluated as exp2 of log2(e)-scaled sums.  Accumulation and
+// the boundary state are fp32.
 #pragma once
 
 #include <climits>
@@ -71,7 +85,14 @@ struct FwdParams {
     int n_xcd;
     int *flags;               // per (sequence, head): published state parts (kWaves per chunk)
     int *error;
+    // H counts kernel heads of P channels.  A head dim wider than the kernel
+    // tile (P = 128 on 64-wide tiles) runs as `hsub` consecutive kernel heads
+    // per model head: x, y and the states are then exactly the layout of
+    // H = hsub * nheads heads of P channels (every state row depends only on
+    // its own channel of x and on the head's shared dt, A, B, C), while dt, A,
+    // D and dt_bias are indexed by the model head h / hsub.
     int H, G;
+    int hsub;                 // kernel heads per model head (1 or 2)
     int heads_per_item;       // head slice length (the last slice of a group may be shorter)
     int slices;               // slices per group: ceil((H / G) / heads_per_item)
 };
@@ -89,6 +110,10 @@ struct FwdShape {
     static constexpr int NP = NK * 32;           // state dim padded to a K step
     static constexpr int QT = Q / 16;            // 16-row tiles of a chunk (<= 2 per wave)
     static constexpr int QK = Q / 32;            // K steps over a chunk
+    static constexpr int BLK = 64;               // tokens per decay block
+    static constexpr int KPB = BLK / 32;         // K steps per decay block
+    static constexpr int TPB = BLK / 16;         // 16-row tiles per decay block
+    static constexpr int NBLK = Q / BLK;
     static constexpr bool kTwoTiles = QT > kWaves;   // waves own tiles w and 2*kWaves-1-w
     static constexpr int GT = kTwoTiles ? QT + 1 : QT; // C B^T tiles held per wave
     // chunk-state work split: WN waves along the state dim, WP along the head dim
@@ -97,45 +122,48 @@ struct FwdShape {
     static constexpr int NTW = (NT + WN - 1) / WN;   // state tiles per wave
     static constexpr int PTW = (PT + WP - 1) / WP;   // head-dim tiles per wave
     static constexpr int E = (int)sizeof(IO);
+    static constexpr int FRAG_REGS = 8 * E / 4;  // registers per MFMA operand fragment
     static constexpr int PAD = 16 / E;           // 16 bytes of padding per LDS row
     static constexpr int SB = NP + PAD;          // row stride of the B chunk
-    static constexpr int SX = Q + PAD;           // row stride of the x^T tile
+    static constexpr int SX = Q + PAD;           // row stride of the x^T tiles
     static constexpr int SH = NP + PAD;          // row stride of the incoming state
     static constexpr int kLdsB = Q * SB * E;
     static constexpr int kLdsX = P * SX * E;
     static constexpr int kLdsH = P * SH * E;
-    static constexpr int kNVec = 7;              // per-token float vectors (+ dt/A staging)
-    static constexpr int kLdsVec = kNVec * Q * 4 + 16;
-    static constexpr int kLds = kLdsB + kLdsX + kLdsH + kLdsVec + 16;
-    static constexpr bool kFits = kLds <= 160 * 1024 && QT <= 2 * kWaves;
+    static constexpr int kNVec = 6;              // per-token float vectors (+ dt/A staging)
+    static constexpr int kLdsVec = kNVec * Q * 4 + 32;
+    static constexpr int kLdsMax = 160 * 1024;
+    // B^T operands of the chunk state kept in registers across the heads of an
+    // item; B is then read from LDS only while the item is set up.
+    static constexpr bool kBtRegs = NTW * QK * FRAG_REGS <= 32;
+    // (the C-in-LDS read-out below needs the B chunk's space to itself)
+    // LDS: [vectors][x^T][xh^T][incoming state][B chunk].  Where that does not
+    // fit, the state tile shares xh^T's space (xh^T is dead once the compute
+    // phase has ended) and/or the B chunk shares the per-head tiles' space
+    // (it is dead once an item is set up, when its B^T operands are in
+    // registers).
+    static constexpr int kHeadSep = 2 * kLdsX + kLdsH;
+    static constexpr bool kCInLdsWanted = kBtRegs;
+    static constexpr int kHeadAl = 2 * kLdsX > kLdsX + kLdsH ? 2 * kLdsX : kLdsX + kLdsH;
+    static constexpr bool kFitSep = kLdsVec + kHeadSep + kLdsB <= kLdsMax;
+    static constexpr bool kFitAliasH = kLdsVec + kHeadAl + kLdsB <= kLdsMax;
+    static constexpr bool kFitAliasB = kBtRegs && kLdsVec + cmax(kHeadSep, kLdsB) <= kLdsMax;
+    static constexpr bool kFitAliasHB = kBtRegs && kLdsVec + cmax(kHeadAl, kLdsB) <= kLdsMax;
+    static constexpr bool kAliasB = !kFitSep && !kFitAliasH && (kFitAliasB || kFitAliasHB);
+    static constexpr bool kAliasH = !kFitSep && (kFitAliasH ? true : !kFitAliasB);
+    static constexpr int kHeadBytes = kAliasH ? kHeadAl : kHeadSep;
+    static constexpr int kOffX = kLdsVec;
+    static constexpr int kOffXh = kOffX + kLdsX;
+    static constexpr int kOffH = kAliasH ? kOffXh : kOffXh + kLdsX;
+    static constexpr int kOffB = kAliasB ? kOffX : kOffX + kHeadBytes;
+    static constexpr int kLds = kAliasB ? kLdsVec + cmax(kHeadBytes, kLdsB) : kLdsVec + kHeadBytes + kLdsB;
+    // C rows for the read-out in the B chunk's LDS (dead once B^T is in registers)
+    static constexpr bool kCInLds = kCInLdsWanted && !kAliasB;
+    static constexpr bool kFits = (kFitSep || kFitAliasH || kFitAliasB || kFitAliasHB) && QT <= 2 * kWaves &&
+                                  Q % BLK == 0;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float exp2f_fast(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// v + (value of v in the lane selected by the DPP control `ctrl`), where lanes
-// without a source (or outside `row_mask`) add 0.
-template <int ctrl, int row_mask>
-__device__ __forceinline__ float dpp_add(float v) {
-    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask, 0xF, true);
-    return v + __builtin_bit_cast(float, t);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: four
-// shifts inside each 16-lane row, then row 0 and 2's last lane into rows 1
-// and 3, then lane 31 into rows 2 and 3.
-__device__ __forceinline__ float wave_inclusive_sum(float v) {
-    v = dpp_add<0x111, 0xF>(v);   // row_shr:1
-    v = dpp_add<0x112, 0xF>(v);   // row_shr:2
-    v = dpp_add<0x114, 0xF>(v);   // row_shr:4
-    v = dpp_add<0x118, 0xF>(v);   // row_shr:8
-    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15
-    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31
-    return v;
-}
 
 // K-slot order.  Every contraction over chunk tokens uses the same slot
 // order: within a 32-token K step, slot e (0..7) of lane group lg holds token
@@ -164,18 +192,6 @@ __device__ __forceinline__ typename Io<IO>::Frag load_bt_frag(const IO *sB, int 
         for (int e = 0; e < 8; ++e) f[e] = sB[(k0 + 16 * (e >> 2) + 4 * lg + (e & 3)) * SB + n0 + li];
     }
     return f;
-}
-
-// Slot-wise scaling of a fragment: slot e by lo[e] (e < 4) or hi[e - 4].
-template <typename IO>
-__device__ __forceinline__ typename Io<IO>::Frag scale_frag(typename Io<IO>::Frag f, f32x4 lo, f32x4 hi) {
-    typename Io<IO>::Frag o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        o[e] = from_f32<IO>(to_f32(f[e]) * lo[e]);
-        o[e + 4] = from_f32<IO>(to_f32(f[e + 4]) * hi[e]);
-    }
-    return o;
 }
 
 // Registers holding one head's x chunk (units of 4 tokens x 8 channels) and,
@@ -219,10 +235,10 @@ struct Prefetch {
 #pragma unroll
             for (int k = 0; k < R; ++k) {
                 const int i = tid * R + k;
-                dt[k] = (i < q) ? prm.dt[(tok0 + i) * prm.H + h] : 0.f;
+                dt[k] = (i < q) ? prm.dt[(tok0 + i) * (prm.H / prm.hsub) + h / prm.hsub] : 0.f;
             }
-            a = prm.A[h];
-            braw = (prm.dtp.bias ? prm.dtp.bias : prm.A)[h];   // branch-free
+            a = prm.A[h / prm.hsub];
+            braw = (prm.dtp.bias ? prm.dtp.bias : prm.A)[h / prm.hsub];   // branch-free
         }
     }
 
@@ -238,22 +254,32 @@ struct Prefetch {
         if (lane == 0) sStage[Q] = a;
     }
 
-    // x^T[p][i .. i+3] from 4 tokens of one channel
-    __device__ __forceinline__ void stage(IO *sX, int tid) const {
+    // x^T[p][i .. i+3] from 4 tokens of one channel, as is into sX and times
+    // the per-token factor into sXh.  fh(k) holds the factor of the scan
+    // lane's k-th token (R consecutive tokens per lane of the wave).
+    template <typename FH>
+    __device__ __forceinline__ void stage(IO *sX, IO *sXh, int tid, FH fh) const {
         typedef typename Io<IO>::Half Half;
 #pragma unroll
         for (int k = 0; k < NU; ++k) {
             const int u = tid + k * S::kThreads;
+            const int t4 = unit_t4(u);
+            const int p0 = unit_p0(u);
+            float fac[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) fac[t] = fh(t % R, (4 * t4 + t) / R);   // every lane shuffles
             if (u < NUNIT) {
-                const int t4 = unit_t4(u);
-                const int p0 = unit_p0(u);
                 const int pos = xpos(4 * t4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    Half v;
+                    Half v, w;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = x[k][t][e];
+                    for (int t = 0; t < 4; ++t) {
+                        v[t] = x[k][t][e];
+                        w[t] = from_f32<IO>(to_f32(x[k][t][e]) * fac[t]);
+                    }
                     *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + pos) = v;
+                    *reinterpret_cast<Half *>(sXh + (p0 + e) * S::SX + pos) = w;
                 }
             }
         }
@@ -272,13 +298,13 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     // that their addresses fit the 16-bit immediate offset of LDS instructions;
     // the B chunk (the largest tile) is last.
     float *vS2 = reinterpret_cast<float *>(smem);  // s * log2(e)
-    IO *sX = reinterpret_cast<IO *>(smem + S::kLdsVec + 16);
-    IO *sH = reinterpret_cast<IO *>(smem + S::kLdsVec + 16 + S::kLdsX);
-    IO *sB = reinterpret_cast<IO *>(smem + S::kLdsVec + 16 + S::kLdsX + S::kLdsH);
+    IO *sX = reinterpret_cast<IO *>(smem + S::kOffX);
+    IO *sXh = reinterpret_cast<IO *>(smem + S::kOffXh);
+    IO *sH = reinterpret_cast<IO *>(smem + S::kOffH);
+    IO *sB = reinterpret_cast<IO *>(smem + S::kOffB);
     float *vDt = vS2 + Q;     // dt_j
     float *vCol = vDt + Q;    // exp(s_r - s_j) dt_j, r = last token of j's 16-tile
-    float *vW = vCol + Q;     // exp(s_last - s_j) dt_j
-    float *vEo = vW + Q;      // exp(s_i)
+    float *vEo = vCol + Q;    // exp(s_i)
     float *vRef = vEo + Q;    // s2 of the last token of each 16-tile (QT used)
     float *sStage = vRef + Q; // next head's dt (Q values) and A, staged by wave 0
     int *sTicket = reinterpret_cast<int *>(sStage + Q + 4);
@@ -369,8 +395,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         load_c(hasB ? Ib : S::QT, cgb);
         if (wave == 0) pf.stage_dt(sStage, lane, q, prm.dtp);
         __syncthreads();  // B chunk and the first head's dt in LDS
-        // Kept in the io precision (the decay-weighted mask built from it is
-        // rounded to the io type for the MFMA anyway); fp32 accumulation.
+        // Kept in the io precision (the MFMAs take them in it); fp32 accumulation.
         Half gtile[S::GT];
     #pragma unroll
         for (int J = 0; J < S::GT; ++J) {
@@ -394,110 +419,147 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
 
         const int wn = wave % S::WN;
         const int wp = wave / S::WN;
+        // B^T operands of the chunk state for this wave's state tiles, all K steps
+        Frag btr[S::kBtRegs ? S::NTW : 1][S::kBtRegs ? S::QK : 1];
+        if constexpr (S::kBtRegs) {
+    #pragma unroll
+            for (int a = 0; a < S::NTW; ++a) {
+                const int nt = wn + a * S::WN;
+    #pragma unroll
+                for (int ks = 0; ks < S::QK; ++ks) {
+                    btr[a][ks] = zero_frag<Frag>();
+                    if (wp < S::PT && nt < S::NT) btr[a][ks] = load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg);
+                }
+            }
+        }
+        // With the B^T operands in registers, the B chunk is dead: its LDS then
+        // holds the chunk's C rows for the read-out (row layout, like B).
+        IO *sC = sB;
+        if constexpr (S::kBtRegs) {
+            __syncthreads();   // every wave is done with the B chunk
+            constexpr int VPR = S::NP * S::E / 16;
+            constexpr int VN = N * S::E / 16;
+            constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
+    #pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int u = tid + k * S::kThreads;
+                const int j = u / VPR;
+                const int c = u - j * VPR;
+                i32x4 v = i32x4{0, 0, 0, 0};
+                if (u < Q * VPR && j < q && c < VN) v = *reinterpret_cast<const i32x4 *>(Cg + j * bs + c * (16 / S::E));
+                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sC + j * S::SB + c * (16 / S::E)) = v;
+            }
+            // (read only after the first head's staging barrier)
+        } else if constexpr (S::kAliasB) {
+            __syncthreads();   // the per-head tiles overwrite the B chunk
+        }
 
-        // Diagonal block of tile I (transposed, Y^T = x^T M^T): accumulator
-        // element r of tile pt is Y_diag[16 I + li][pt*16 + 4*lg + r].  `fromA`
-        // selects which end of gtile holds the tile's C B^T row.  The LDS
-        // operands of K step kj+1 are read before step kj's arithmetic (the
-        // scheduling barriers keep that order); sref holds the 16-tile
-        // reference cumsums in scalar registers.
-        auto diag_block = [&](auto from_a, int I, f32x4 (&accY)[S::PT], const float (&sref)[S::QT]) {
+        // C B^T fragment (rows of tile I, K step ks) straight from the
+        // registers, for the blocks left of the row's own decay block.
+        auto cb_frag = [&](auto from_a, int ks) {
+            constexpr bool fromA = decltype(from_a)::value;
+            Frag m;
+    #pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int jt = 2 * ks + half;
+                const Half &gh = gtile[fromA ? jt : S::GT - 1 - jt];
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) m[4 * half + r] = gh[r];
+            }
+            return m;
+        };
+        // Decay-weighted mask fragment of tile I, K step ks, inside the row's
+        // own decay block: lane holds M[i_row][j], j = 32 ks + 16 half + 4 lg + r.
+        // Below the diagonal 16-tile: G * exp(s_i - s_r) * exp(s_r - s_j) dt_j
+        // (both factors <= 1, r the last token of j's 16-tile); on it the exact
+        // exp(s_i - s_j) with a causal select.
+        auto mask_frag = [&](auto from_a, int I, int ks, float s2_i, const float (&sref)[S::QT]) {
             constexpr bool fromA = decltype(from_a)::value;
             const int i_row = 16 * I + li;
-            const float s2_i = vS2[i_row];
+            Frag m;
     #pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt) accY[pt] = zero4();
-            Frag xf[2][S::PT];
-            f32x4 colv[2][2];
-            auto load_step = [&](int kj, Frag (&xo)[S::PT], f32x4 (&co)[2]) {
+            for (int half = 0; half < 2; ++half) {
+                const int jt = 2 * ks + half;
+                const int j0 = 32 * ks + 16 * half + 4 * lg;
+                const Half &gh = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
+                f32x4 gv;
     #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt)
-                    xo[pt] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + 32 * kj + 8 * lg);
+                for (int r = 0; r < 4; ++r) gv[r] = to_f32(gh[r]);
+                if (jt < I) {
+                    const float rowf = exp2f_fast(s2_i - sref[jt]);
+                    const f32x4 colv = *reinterpret_cast<const f32x4 *>(vCol + j0);
     #pragma unroll
-                for (int half = 0; half < 2; ++half)
-                    co[half] = *reinterpret_cast<const f32x4 *>(vCol + 32 * kj + 16 * half + 4 * lg);
-            };
-            load_step(0, xf[0], colv[0]);
-    #pragma unroll
-            for (int kj = 0; kj < S::QT / 2; ++kj) {
-                if (kj > I / 2) break;
-                const int cur = kj & 1;
-                if (kj + 1 < S::QT / 2 && kj + 1 <= I / 2) load_step(kj + 1, xf[cur ^ 1], colv[cur ^ 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                Frag m;  // lane holds M[i_row][j], j = 32 kj + 16 half + 4 lg + r
-    #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int jt = 2 * kj + half;
-                    const int j0 = 32 * kj + 16 * half + 4 * lg;
-                    const Half &gh = gtile[fromA ? jt : S::GT - 1 - jt];   // C B^T tile (I, jt)
-                    f32x4 gv;
-    #pragma unroll
-                    for (int r = 0; r < 4; ++r) gv[r] = to_f32(gh[r]);
-                    if (jt < I) {
-                        const float rowf = exp2f_fast(s2_i - sref[jt]);
-    #pragma unroll
-                        for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * colv[cur][half][r]);
-                    } else if (jt == I) {
-                        const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
-                        const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
-    #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
-                            m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
-                        }
-                    } else {
-    #pragma unroll
-                        for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(0.f);
-                    }
-                }
-    #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt) accY[pt] = Io<IO>::mfma(accY[pt], xf[cur][pt], m);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        // State read-out (H C^T) and the final combination of tile I.
-        auto finish_tile = [&](int I, const Frag (&cf)[S::NK], const f32x4 (&accY)[S::PT], IO *yg, float Dh) {
-            const int i_row = 16 * I + li;
-            f32x4 accO[S::PT];
-    #pragma unroll
-            for (int pt = 0; pt < S::PT; ++pt) accO[pt] = zero4();
-            // software pipeline: the H fragments of K step ks+1 are read while the
-            // MFMAs of step ks run (the scheduling barriers keep that order)
-            Frag hf[2][S::PT];
-            auto load_h = [&](int ks, Frag (&o)[S::PT]) {
-    #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt)
-                    o[pt] = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
-            };
-            load_h(0, hf[0]);
-    #pragma unroll
-            for (int ks = 0; ks < S::NK; ++ks) {
-                if (ks + 1 < S::NK) load_h(ks + 1, hf[(ks + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt) accO[pt] = Io<IO>::mfma(accO[pt], hf[ks & 1][pt], cf[ks]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (i_row < q) {
-                const float eo = vEo[i_row];
-                float xv[S::PT][4];   // x[i_row][pt*16 + 4 lg + r], all read before use
-                const int xp = xpos(i_row);
-    #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt)
-    #pragma unroll
-                    for (int r = 0; r < 4; ++r) xv[pt][r] = to_f32(sX[(pt * 16 + 4 * lg + r) * S::SX + xp]);
-                __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                for (int pt = 0; pt < S::PT; ++pt) {
-                    Half yv;
+                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(gv[r] * rowf * colv[r]);
+                } else if (jt == I) {
+                    const f32x4 s2j = *reinterpret_cast<const f32x4 *>(vS2 + j0);
+                    const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float xval = xv[pt][r];
-                        yv[r] = from_f32<IO>(accY[pt][r] + eo * accO[pt][r] + Dh * xval);
+                        const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
+                        m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
                     }
-                    *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
+                } else {
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) m[4 * half + r] = from_f32<IO>(0.f);
                 }
             }
+            return m;
+        };
+        // x^T[pt*16 + 4 lg + r][16 I + li], r = 0..3, for the skip term: one
+        // transposing read per head-dim tile (lane 4e + c of a 16-lane group
+        // points at row pt*16 + 4 lg + e, tokens 16 I + 4c .. 4c + 3, which sit
+        // at consecutive positions of the K-slot order).
+        auto x_rows = [&](int I, int pt) -> f32x4 {
+            f32x4 v;
+            if constexpr (sizeof(IO) == 2) {
+                const int e = li >> 2, c = li & 3;
+                const bf16x4 t = lds_read_tr16(reinterpret_cast<const bf16 *>(
+                    sX + (pt * 16 + 4 * lg + e) * S::SX + 32 * (I >> 1) + 8 * c + 4 * (I & 1)));
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = to_f32(t[r]);
+            } else {
+                const int xp = xpos(16 * I + li);
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = sX[(pt * 16 + 4 * lg + r) * S::SX + xp];
+            }
+            return v;
+        };
+        // Runs f with this wave's index as a compile-time constant, so that the
+        // phases below are unrolled without any branch on the wave's row tiles.
+        auto with_wave = [&](auto f) {
+            static_assert(S::kWaves == 8, "one case per wave");
+            switch (wave) {
+            case 0: f(std::integral_constant<int, 0>{}); break;
+            case 1: f(std::integral_constant<int, 1>{}); break;
+            case 2: f(std::integral_constant<int, 2>{}); break;
+            case 3: f(std::integral_constant<int, 3>{}); break;
+            case 4: f(std::integral_constant<int, 4>{}); break;
+            case 5: f(std::integral_constant<int, 5>{}); break;
+            case 6: f(std::integral_constant<int, 6>{}); break;
+            default: f(std::integral_constant<int, 7>{}); break;
+            }
+        };
+        // Row tiles of wave W: tile a = W, tile b = 2 kWaves - 1 - W (chunks of
+        // 2 kWaves tiles); each tile's decay block R, and its explicit K steps
+        // [KPB R, I / 2] (the steps before them run on the C B^T tiles as is).
+        struct WaveTiles {
+            int IA, IB, RA, RB, EA0, EA1, EB0, EB1;
+            bool HA, HB;
+        };
+        auto tiles_of = [](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            WaveTiles t{};
+            t.IA = W;
+            t.IB = 2 * S::kWaves - 1 - W;
+            t.HA = W < S::QT;
+            t.HB = S::kTwoTiles;
+            t.RA = t.IA / S::TPB;
+            t.RB = t.IB / S::TPB;
+            t.EA0 = S::KPB * t.RA;
+            t.EA1 = t.IA / 2;
+            t.EB0 = S::KPB * t.RB;
+            t.EB1 = t.IB / 2;
+            return t;
         };
 
         int *sReady = sTicket + 1;
@@ -520,8 +582,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             IO *yg = reinterpret_cast<IO *>(prm.y) + tok0 * xs + h * P;
             const int unit = seq * H + h;
 
-            // ---- (1) stage x^T; in-chunk cumulative sum and per-token vectors ----
-            pf.stage(sX, tid);
+            // ---- (1) in-chunk cumulative sum, per-token vectors, x^T and xh^T ----
             {
                 // one early look at the predecessor's flag (the state loads can
                 // then be issued before the compute phase)
@@ -547,10 +608,13 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 const float excl = wave_inclusive_sum(run) - run;
     #pragma unroll
                 for (int k = 0; k < R; ++k) s2[k] = (excl + s2[k]) * kLog2e;
-                const float s2_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s2[R - 1]), 63));
-                // last token of each 16-token tile: index (i | 15), held by lane ((i | 15) / R)
-                const int ref_lane = ((lane * R) | 15) / R;
-                const float ref = __shfl(s2[R - 1], ref_lane, 64);
+                // last token of each 16-token tile: index (i | 15), held by lane ((i | 15) / R);
+                // likewise the last token of each 64-token decay block
+                const float ref = __shfl(s2[R - 1], ((lane * R) | 15) / R, 64);
+                const float ref64 = __shfl(s2[R - 1], ((lane * R) | (S::BLK - 1)) / R, 64);
+                float fh[R];   // staging factor of xh: exp(e_b - s_j) dt_j
+    #pragma unroll
+                for (int k = 0; k < R; ++k) fh[k] = exp2f_fast(ref64 - s2[k]) * dtv[k];
                 if ((lane >> 3) == wave) {
     #pragma unroll
                     for (int k = 0; k < R; ++k) {
@@ -559,25 +623,17 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                         vS2[i] = s2[k];
                         vDt[i] = d;
                         vCol[i] = exp2f_fast(ref - s2[k]) * d;
-                        vW[i] = exp2f_fast(s2_end - s2[k]) * d;
                         vEo[i] = exp2f_fast(s2[k]);
                         if ((i & 15) == 15) vRef[i >> 4] = s2[k];
                     }
                 }
+                pf.stage(sX, sXh, tid, [&](int k, int src) { return __shfl(fh[k], src, 64); });
                 asm volatile("" : "+v"(flagv));   // keeps the comparison (and its wait) here
                 if (wave == 0 && lane == 0) *sReady = flagv >= S::kWaves * cloc;
-            }
-            if constexpr (S::NP != N) {
-                for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
-                    const int p = v / (S::NP - N);
-                    sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
-                }
             }
             __syncthreads();
             const float s2_last = vS2[Q - 1];
             const bool early = *sReady != 0;
-            // the next head's x and dt load while this head is computed
-            if (h + 1 < h_end) pf.load(prm, tok0, q, h + 1, tid);
 
             // incoming boundary state, issued now
             // when the predecessor had already published, else after the wait below
@@ -604,85 +660,133 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                                 rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kStateLoad));
                     }
             };
-            if (early) load_state();
 
             // ---- (2) compute: chunk state and both tiles' diagonal blocks ----
-            // S_c^T = (B^T o w) x : N x P, K = chunk; accumulator element r of tile
-            // (nt, pt) is S_c[p][n] with p = pt*16 + li and n = nt*16 + 4*lg + r.
+            // One pass over the K steps.  Each step reads the xh^T fragments of
+            // every head-dim tile once, for the chunk state and for the rows whose
+            // decay block lies right of the step; rows inside their own block
+            // take the x^T fragments and the explicit mask instead.  The next
+            // step's xh^T (and B^T) fragments are read while the current step's
+            // MFMAs run (the scheduling barriers keep that order).
+            // S_c^T = B^T xh: accumulator element r of tile (nt, pt) is S_c[p][n]
+            // with p = pt*16 + li and n = nt*16 + 4*lg + r.  Diagonal blocks are
+            // computed transposed (Y^T = x^T M^T): element r of tile pt is
+            // Y_diag[16 I + li][pt*16 + 4*lg + r].
+            float sref[S::QT];   // 16-tile reference cumsums, wave-uniform
+    #pragma unroll
+            for (int t = 0; t < S::QT; ++t)
+                sref[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, vRef[t])));
             f32x4 accS[S::NTW][S::PTW];
     #pragma unroll
             for (int a = 0; a < S::NTW; ++a)
     #pragma unroll
                 for (int b = 0; b < S::PTW; ++b) accS[a][b] = zero4();
-            auto chunk_state = [&]() {
-            if (wp < S::PT) {
-                // software pipeline: the operands of K step ks+1 are read while
-                // step ks is scaled and multiplied
-                struct ScOps {
-                    f32x4 wlo, whi;
-                    Frag xf[S::PTW];
-                    Frag bt[S::NTW];
-                };
-                auto load_sc = [&](int ks, ScOps &o) {
-                    o.wlo = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 4 * lg);
-                    o.whi = *reinterpret_cast<const f32x4 *>(vW + ks * 32 + 16 + 4 * lg);
+            f32x4 accYa[S::PT], accYb[S::PT];
     #pragma unroll
-                    for (int b = 0; b < S::PTW; ++b) {
-                        const int pt = wp + b * S::WP;
-                        o.xf[b] = zero_frag<Frag>();
-                        if (pt < S::PT)
-                            o.xf[b] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
-                    }
+            for (int pt = 0; pt < S::PT; ++pt) {
+                accYa[pt] = zero4();
+                accYb[pt] = zero4();
+            }
+            auto scale4 = [](f32x4 (&acc)[S::PT], float f) {
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt)
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[pt][r] *= f;
+            };
+            with_wave([&](auto wc) {
+                constexpr int W = decltype(wc)::value;
+                constexpr WaveTiles T = tiles_of(wc);
+                constexpr int WNc = W % S::WN, WPc = W / S::WN;
+                constexpr bool HS = WPc < S::PT;   // the wave has chunk-state tiles
+                const float s2_ia = T.HA ? vS2[16 * T.IA + li] : 0.f;
+                const float s2_ib = T.HB ? vS2[16 * T.IB + li] : 0.f;
+                Frag xh[2][S::PT];
+                Frag bt[2][S::NTW];
+                auto load_step = [&](int ks, Frag (&xo)[S::PT], Frag (&bo)[S::NTW]) {
+    #pragma unroll
+                    for (int pt = 0; pt < S::PT; ++pt)
+                        xo[pt] = *reinterpret_cast<const Frag *>(sXh + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
     #pragma unroll
                     for (int a = 0; a < S::NTW; ++a) {
-                        const int nt = wn + a * S::WN;
-                        o.bt[a] = zero_frag<Frag>();
-                        if (nt < S::NT) o.bt[a] = load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg);
+                        const int nt = WNc + a * S::WN;
+                        if constexpr (S::kBtRegs) bo[a] = btr[a][ks];
+                        else bo[a] = (HS && nt < S::NT) ? load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg)
+                                                        : zero_frag<Frag>();
                     }
                 };
-                ScOps ops[2];
-                load_sc(0, ops[0]);
+                load_step(0, xh[0], bt[0]);
     #pragma unroll
                 for (int ks = 0; ks < S::QK; ++ks) {
                     const int cur = ks & 1;
-                    if (ks + 1 < S::QK) load_sc(ks + 1, ops[cur ^ 1]);
+                    const int blk = ks / S::KPB;
+                    if (ks + 1 < S::QK) load_step(ks + 1, xh[cur ^ 1], bt[cur ^ 1]);
                     __builtin_amdgcn_sched_barrier(0);
+                    // x^T fragments of the rows whose own block this step is in
+                    const bool exA = T.HA && ks >= T.EA0 && ks <= T.EA1;
+                    const bool exB = T.HB && ks >= T.EB0 && ks <= T.EB1;
+                    Frag xea[S::PT], xeb[S::PT];
     #pragma unroll
-                    for (int a = 0; a < S::NTW; ++a) {
-                        const int nt = wn + a * S::WN;
-                        if (nt < S::NT) {
-                            const Frag bt = scale_frag<IO>(ops[cur].bt[a], ops[cur].wlo, ops[cur].whi);
+                    for (int pt = 0; pt < S::PT; ++pt) {
+                        if (exA) xea[pt] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                        if (exB) xeb[pt] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                    }
+                    if (ks % S::KPB == 0 && blk > 0) {
+                        // block decay exp(e_b - e_{b-1}) on every sum still in its recurrence
+                        const float dl = exp2f_fast(sref[S::TPB * blk + S::TPB - 1] - sref[S::TPB * blk - 1]);
+    #pragma unroll
+                        for (int a = 0; a < S::NTW; ++a)
+    #pragma unroll
+                            for (int b = 0; b < S::PTW; ++b)
+    #pragma unroll
+                                for (int r = 0; r < 4; ++r) accS[a][b][r] *= dl;
+                        if (T.HA && blk < T.RA) scale4(accYa, dl);
+                        if (T.HB && blk < T.RB) scale4(accYb, dl);
+                    }
+                    // entering the row's own block: the row factor exp(s_i - e_{R-1})
+                    if (T.HA && T.RA > 0 && ks == T.EA0) scale4(accYa, exp2f_fast(s2_ia - sref[S::TPB * T.RA - 1]));
+                    if (T.HB && T.RB > 0 && ks == T.EB0) scale4(accYb, exp2f_fast(s2_ib - sref[S::TPB * T.RB - 1]));
+                    if (HS) {
+    #pragma unroll
+                        for (int a = 0; a < S::NTW; ++a)
     #pragma unroll
                             for (int b = 0; b < S::PTW; ++b) {
-                                const int pt = wp + b * S::WP;
-                                if (pt < S::PT) accS[a][b] = Io<IO>::mfma(accS[a][b], bt, ops[cur].xf[b]);
+                                const int pt = WPc + b * S::WP;
+                                if (WNc + a * S::WN < S::NT && pt < S::PT)
+                                    accS[a][b] = Io<IO>::mfma(accS[a][b], bt[cur][a], xh[cur][pt]);
                             }
-                        }
+                    }
+                    if (T.HA && ks < T.EA0) {
+                        const Frag m = cb_frag(std::true_type{}, ks);
+    #pragma unroll
+                        for (int pt = 0; pt < S::PT; ++pt) accYa[pt] = Io<IO>::mfma(accYa[pt], xh[cur][pt], m);
+                    }
+                    if (T.HB && ks < T.EB0) {
+                        const Frag m = cb_frag(std::false_type{}, ks);
+    #pragma unroll
+                        for (int pt = 0; pt < S::PT; ++pt) accYb[pt] = Io<IO>::mfma(accYb[pt], xh[cur][pt], m);
+                    }
+                    if (exA) {
+                        const Frag m = mask_frag(std::true_type{}, T.IA, ks, s2_ia, sref);
+    #pragma unroll
+                        for (int pt = 0; pt < S::PT; ++pt) accYa[pt] = Io<IO>::mfma(accYa[pt], xea[pt], m);
+                    }
+                    if (exB) {
+                        const Frag m = mask_frag(std::false_type{}, T.IB, ks, s2_ib, sref);
+    #pragma unroll
+                        for (int pt = 0; pt < S::PT; ++pt) accYb[pt] = Io<IO>::mfma(accYb[pt], xeb[pt], m);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-            };
-            // The two waves that share a SIMD (w and w + kWaves/2) take the
-            // MFMA-dense chunk state and the VALU-dense diagonal blocks in
-            // opposite orders, so that one's matrix work overlaps the other's
-            // vector work.
-            const bool sc_first = wave < S::kWaves / 2;
-            if (sc_first) chunk_state();
-            f32x4 accYa[S::PT], accYb[S::PT];
-            float sref[S::QT];   // 16-tile reference cumsums, wave-uniform
-    #pragma unroll
-            for (int t = 0; t < S::QT; ++t)
-                sref[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, vRef[t])));
-            if (hasA) diag_block(std::true_type{}, Ia, accYa, sref);
-            if (hasB) diag_block(std::false_type{}, Ib, accYb, sref);
-            if (!sc_first) chunk_state();
+            });
 
-            Frag cfa[S::NK];
-            if (hasA) load_c(Ia, cfa);
             // ---- (3) chain: wait if needed, H_{c+1} = exp(s_last) H_c + S_c, H_c to LDS ----
-            if (!early) {
-                if (tid == 0) {
+            // One thread waits for the predecessor's counter; the incoming state's
+            // loads are then issued before the next head's x and dt prefetch:
+            // loads complete in order, so waiting for the state never waits for
+            // the prefetch.
+            if (early) load_state();
+            if (!early || S::kAliasH) {
+                if (!early && tid == 0) {
                     int it = 0;
                     while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                            S::kWaves * cloc) {
@@ -693,14 +797,18 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                         }
                     }
                 }
+                // (also: with the state tile over xh^T, every wave has left the compute phase)
                 __syncthreads();
-                load_state();
+                if (!early) load_state();
+            }
+            if (h + 1 < h_end) pf.load(prm, tok0, q, h + 1, tid);
+            Frag cfa[S::kCInLds ? 1 : S::NK], cfb[S::kCInLds ? 1 : S::NK];
+            if constexpr (!S::kCInLds) {
+                load_c(hasA ? Ia : S::QT, cfa);
+                load_c(hasB ? Ib : S::QT, cfb);
             }
             const float alpha = exp2f_fast(s2_last);
-            const float Dh = prm.D ? prm.D[h] : 0.f;   // needed only by the epilogue
-            // every load issued so far (state, C rows of tile Ia, D) completes here, on
-            // all paths, so the read-out below only waits for what is issued later
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            const float Dh = prm.D ? prm.D[h / prm.hsub] : 0.f;   // needed only by the epilogue
             if (wp < S::PT) {
                 const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
     #pragma unroll
@@ -724,18 +832,76 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                         }
                     }
             }
+            if constexpr (S::NP != N) {   // zero K slots past the state dim
+                for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
+                    const int p = v / (S::NP - N);
+                    sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
+                }
+            }
             __syncthreads();  // H_c is in LDS
 
             // ---- (4) state read-out and outputs of both tiles ----
-            // Each wave publishes its part of H_{c+1} (one increment of the
-            // (sequence, head) counter) once its state stores are acknowledged;
-            // a successor waits for all kWaves increments.
-            Frag cfb[S::NK];
-            if (hasB) load_c(Ib, cfb);
-            if (hasA) finish_tile(Ia, cfa, accYa, yg, Dh);
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
-            if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (hasB) finish_tile(Ib, cfb, accYb, yg, Dh);
+            // Y_off = C H_c^T for both row tiles in one pass over the state's K
+            // steps (each H fragment is read once); then each wave publishes its
+            // part of H_{c+1} (one increment of the (sequence, head) counter) once
+            // its state stores are acknowledged -- a successor waits for all
+            // kWaves increments -- and writes y = Y_diag + exp(s_i) Y_off + D x.
+            with_wave([&](auto wc) {
+                constexpr WaveTiles T = tiles_of(wc);
+                f32x4 oa[S::PT], ob[S::PT];
+    #pragma unroll
+                for (int pt = 0; pt < S::PT; ++pt) {
+                    oa[pt] = zero4();
+                    ob[pt] = zero4();
+                }
+                Frag hf[2][S::PT];
+                Frag ca[2], cb[2];
+                auto load_h = [&](int ks, Frag (&o)[S::PT], Frag &oa_, Frag &ob_) {
+    #pragma unroll
+                    for (int pt = 0; pt < S::PT; ++pt)
+                        o[pt] = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
+                    if constexpr (S::kCInLds) {
+                        if (T.HA) oa_ = *reinterpret_cast<const Frag *>(sC + (16 * T.IA + li) * S::SB + ks * 32 + 8 * lg);
+                        if (T.HB) ob_ = *reinterpret_cast<const Frag *>(sC + (16 * T.IB + li) * S::SB + ks * 32 + 8 * lg);
+                    } else {
+                        oa_ = cfa[S::kCInLds ? 0 : ks];
+                        ob_ = cfb[S::kCInLds ? 0 : ks];
+                    }
+                };
+                if (T.HA || T.HB) load_h(0, hf[0], ca[0], cb[0]);
+    #pragma unroll
+                for (int ks = 0; ks < S::NK; ++ks) {
+                    if (!(T.HA || T.HB)) break;
+                    if (ks + 1 < S::NK) load_h(ks + 1, hf[(ks + 1) & 1], ca[(ks + 1) & 1], cb[(ks + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int pt = 0; pt < S::PT; ++pt) {
+                        if (T.HA) oa[pt] = Io<IO>::mfma(oa[pt], hf[ks & 1][pt], ca[ks & 1]);
+                        if (T.HB) ob[pt] = Io<IO>::mfma(ob[pt], hf[ks & 1][pt], cb[ks & 1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
+                if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                auto epilogue = [&](int I, const f32x4 (&o)[S::PT], const f32x4 (&accY)[S::PT]) {
+                    const int i_row = 16 * I + li;
+                    f32x4 xv[S::PT];
+    #pragma unroll
+                    for (int pt = 0; pt < S::PT; ++pt) xv[pt] = x_rows(I, pt);
+                    const float eo = vEo[i_row];
+                    if (i_row < q) {
+    #pragma unroll
+                        for (int pt = 0; pt < S::PT; ++pt) {
+                            Half yv;
+    #pragma unroll
+                            for (int r = 0; r < 4; ++r) yv[r] = from_f32<IO>(accY[pt][r] + eo * o[pt][r] + Dh * xv[pt][r]);
+                            *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
+                        }
+                    }
+                };
+                if (T.HA) epilogue(T.IA, oa, accYa);
+                if (T.HB) epilogue(T.IB, ob, accYb);
+            });
             if (wave == 0 && h + 1 < h_end) pf.stage_dt(sStage, lane, q, prm.dtp);   // the next head's dt and A
             __syncthreads();  // every wave is done with this head's LDS tiles
         }

@@ -45,10 +45,10 @@ static bool fwd_try_n(SSD_FWD_PARAMS) {
            fwd_try_q<IO, P, 256>(SSD_FWD_ARGS);
 }
 
+// Kernel head dims 16, 32 and 64 (head dim 128 runs as two kernel heads of 64).
 template <typename IO>
 static bool fwd_dispatch(SSD_FWD_PARAMS) {
-    return fwd_try_n<IO, 16>(SSD_FWD_ARGS) || fwd_try_n<IO, 32>(SSD_FWD_ARGS) || fwd_try_n<IO, 64>(SSD_FWD_ARGS) ||
-           fwd_try_n<IO, 128>(SSD_FWD_ARGS);
+    return fwd_try_n<IO, 16>(SSD_FWD_ARGS) || fwd_try_n<IO, 32>(SSD_FWD_ARGS) || fwd_try_n<IO, 64>(SSD_FWD_ARGS);
 }
 
 }  // namespace ssd

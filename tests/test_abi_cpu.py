@@ -72,16 +72,17 @@ def test_workspace_size_query(lib):
     assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=48)), 256, ssd.SSD_BF16) == 0
     assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims()), 128, ssd.SSD_F32) > 0
     assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=16, dstate=16)), 64, ssd.SSD_F32) > 0
-    # every head dim in {16, 32, 64, 128} and state dim in {16, ..., 256} is built
-    # at the chunk lengths whose tiles fit in LDS
-    for P in (16, 32, 64, 128):
-        for N in (16, 32, 64, 128, 256):
-            assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=P, dstate=N)), 64,
-                                                         ssd.SSD_BF16) > 0, (P, N)
-    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=128)), 128, ssd.SSD_BF16) > 0
-    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=64, dstate=256)), 128, ssd.SSD_BF16) > 0
-    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=256)), 128, ssd.SSD_BF16) == 0
-    assert lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=256)), 64, ssd.SSD_F32) == 0
+    # every head dim in {16, 32, 64, 128}, state dim in {16, ..., 256} and chunk
+    # length in {64, 128, 256} is accepted in both dtypes (a chunk whose tiles
+    # exceed LDS runs as the largest shorter chunk that fits; a shorter chunk
+    # needs a larger schedule, never a smaller one)
+    for io in (ssd.SSD_BF16, ssd.SSD_F32):
+        for P in (16, 32, 64, 128):
+            for N in (16, 32, 64, 128, 256):
+                sizes = [lib.ssd_chunk_scan_fwd_workspace_size(ctypes.byref(_dims(headdim=P, dstate=N)), Q, io)
+                         for Q in (64, 128, 256)]
+                assert min(sizes) > 0, (io, P, N, sizes)
+                assert sizes[0] >= sizes[1] >= sizes[2], (io, P, N, sizes)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -92,8 +93,7 @@ def test_workspace_size_query(lib):
     (dict(dims=_dims(nseq=3)), 2),                               # dense needs nseq == batch
     (dict(Q=100), 4),
     (dict(dims=_dims(headdim=48)), 4),
-    (dict(dims=_dims(dstate=256)), 4),                           # bf16 tiles exceed LDS at Q=256
-    (dict(dims=_dims(headdim=128)), 4),                          # likewise
+    (dict(dims=_dims(dstate=48)), 4),                            # state dim not built
     (dict(dims=_dims(headdim=256)), 4),                          # head dim not built
     (dict(x=None), 1),
     (dict(A=None), 1),
@@ -114,9 +114,9 @@ def test_varlen_validation(lib):
     assert _fwd(lib, _dims(), cu=FAKE + (20 << 30)) == 2
     # and nseq <= 65536
     assert _fwd(lib, _dims(batch=1, nseq=70000), cu=FAKE + (20 << 30)) == 2
-    # a packed batch whose tiles do not fit is reported as unsupported, not
-    # as a layout error (the binding relies on this to name the reason)
-    assert _fwd(lib, _dims(batch=1, nseq=5, headdim=128, dstate=128), io=ssd.SSD_F32,
+    # a packed batch of a size that is not built is reported as unsupported,
+    # not as a layout error (the binding relies on this to name the reason)
+    assert _fwd(lib, _dims(batch=1, nseq=5, headdim=48, dstate=128), io=ssd.SSD_F32,
                 cu=FAKE + (20 << 30)) == 4
 
 
