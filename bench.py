@@ -11,8 +11,10 @@ The roofline object reports the fused forward kernel against HBM bandwidth
 (its algorithmic bytes are the compulsory traffic; see the design doc for the
 per-token figures) and, in "mfma", its algorithmic bf16 MFMA rate.  The
 "cpu_baseline" is the fp64 oracle timed on this host's cores over the whole
-workload.  A decode line for the b256 H80 P64 N128 single-token step is
-included under "decode", and the block prologue (causal convolution of the
+workload.  The 130M-layer shape and the packed
+variable-length batch are reported under "workloads" (parity configurations;
+the headline line is the 2.7B layer).  A decode line for the b256 H80 P64 N128
+single-token step is included under "decode", and the block prologue (causal convolution of the
 fused x|B|C projection) and epilogue (gated RMSNorm) at the same 2.7B layer
 shape under "block" (skip with --no-block), and the backward pass
 (ssd_chunk_scan_bwd, all gradients) at the forward's workload under
@@ -38,20 +40,28 @@ FWD_INDEX = 2                  # Mamba-2 2.7B layer shape
 DEC_INDEX = 4                  # decode, b256
 
 
-def fwd_algorithmic(w):
+def fwd_algorithmic(w, lengths=None, init_state=True):
     """Algorithmic bytes and MFMA flops of one forward pass.
 
-    Bytes: the compulsory HBM traffic -- read x, dt, B, C, the initial state,
-    write y and the final state (A, D negligible).
-    Flops per (token, head): the causal half of the diagonal block
-    2*(Q+1)/2*P, the chunk-state formation 2*N*P and the state read-out
-    2*N*P; per (token, group): the causal half of C B^T, 2*(Q+1)/2*N."""
-    b, L, H, P, N, G, Q = (w["batch"], w["seqlen"], w["nheads"], w["headdim"], w["dstate"],
-                           w["ngroups"], w["chunk"])
-    tok = b * L
+    Bytes: the compulsory HBM traffic -- read x, dt, B, C (and the initial
+    state when there is one), write y and the final state (A, D negligible).
+    Flops, per chunk of q tokens (the last chunk of a sequence may be
+    partial): per head, the causal half of the diagonal block q (q+1) P, and
+    per token the chunk-state formation 2 N P and the state read-out 2 N P;
+    per group, the causal half of C B^T, q (q+1) N.  ``lengths`` lists the
+    sequence lengths of a packed batch (default: batch x seqlen)."""
+    H, P, N, G, Q = w["nheads"], w["headdim"], w["dstate"], w["ngroups"], w["chunk"]
+    if lengths is None:
+        lengths = [w["seqlen"]] * w["batch"]
+    tok = int(sum(lengths))
+    nseq = len(lengths)
     io = 2
-    byts = tok * (H * P * io * 2 + H * 4 + G * N * io * 2) + 2 * b * H * P * N * 4
-    flops = tok * H * (2 * (Q + 1) / 2 * P + 4 * N * P) + tok * G * (2 * (Q + 1) / 2 * N)
+    byts = tok * (H * P * io * 2 + H * 4 + G * N * io * 2) + (2 if init_state else 1) * nseq * H * P * N * 4
+    pairs = 0
+    for L in lengths:
+        full, rest = divmod(int(L), Q)
+        pairs += full * Q * (Q + 1) // 2 + rest * (rest + 1) // 2
+    flops = 2 * pairs * (H * P + G * N) + tok * H * 4 * N * P
     return float(byts), float(flops)
 
 
@@ -146,6 +156,52 @@ def bench_backward(w, stream, x, dt, A, B, C, D, h0):
            "workspace_bytes": int(ws.numel())}
     del ws
     return res
+
+
+def bench_other_forward(stream, to_dev):
+    """The Mamba-2 130M layer shape and the packed variable-length batch:
+    time per call (HIP events over 20 calls on the launch stream), tokens/s,
+    and the algorithmic HBM and MFMA rates against the MI355X peaks."""
+    import torch
+    from selective_state_space_71_amd import ssd, workloads as wl
+    res = {}
+    for idx, label in ((1, "mamba2_130m_layer: batch 8, L 2048, H 24, P 64, N 128, G 1, chunk 256, bf16"),
+                       (3, "varlen_packed: 16 sequences, 65,536 tokens, H 32, P 64, N 128, G 8, chunk 256, bf16")):
+        w = wl.WORKLOADS[idx]
+        inp = wl.workload_inputs(idx)
+        x, B, C = (to_dev(inp[k], True) for k in ("x", "B", "C"))
+        dt, A, D = (to_dev(inp[k], False) for k in ("dt", "A", "D"))
+        h0 = to_dev(inp["init_state"], False) if inp.get("init_state") is not None else None
+        cu_np = inp.get("cu_seqlens")
+        cu = torch.from_numpy(cu_np.astype(np.int32)).to(x.device) if cu_np is not None else None
+        ssd.chunk_scan_fwd(x, dt, A, B, C, D, chunk_len=w["chunk"], init_state=h0, cu_seqlens=cu, check=True)
+        ws = ssd.chunk_scan_fwd.last_workspace
+        y = torch.empty_like(x)
+        us = time_calls(lambda: ssd.chunk_scan_fwd(x, dt, A, B, C, D, chunk_len=w["chunk"], init_state=h0,
+                                                   cu_seqlens=cu, y=y, workspace=ws), stream, nrep=20)
+        assert ssd.check_workspace(ws) == 0
+        lengths = None if cu_np is None else [int(cu_np[i + 1] - cu_np[i]) for i in range(len(cu_np) - 1)]
+        wv = dict(w, seqlen=w.get("seqlen", 0), batch=w.get("batch", 1))
+        byts, flops = fwd_algorithmic(wv, lengths=lengths, init_state=h0 is not None)
+        tok = x.shape[0] * x.shape[1]
+        gbs = byts / (us * 1e-6) / 1e9
+        tfl = flops / (us * 1e-6) / 1e12
+        res[w["name"]] = {"workload": label, "us": us, "tokens_per_s": tok / (us * 1e-6),
+                          "alg_bytes": byts, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "alg_flops": flops, "achieved_tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS}
+        del x, B, C, dt, A, D, h0, cu, ws, y
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_source_sha():
@@ -272,6 +328,8 @@ def main():
         "wall_s_timed": wall,
     }
 
+    out["workloads"] = bench_other_forward(stream, to_dev)
+
     if not args.no_decode:
         wd = wl.WORKLOADS[DEC_INDEX]
         di = wl.workload_inputs(DEC_INDEX)
@@ -305,18 +363,39 @@ def main():
 
     if not args.no_cpu_baseline:
         from oracle import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-        x64 = wl.as_f64(inp["x"], "bf16")
-        B64 = wl.as_f64(inp["B"], "bf16")
-        C64 = wl.as_f64(inp["C"], "bf16")
-        t = time.perf_counter()
-        oracle.ssd_fwd(x64, inp["dt"], inp["A"], B64, C64, inp["D"], init_state=inp["init_state"],
-                       nthreads=threads)
-        cpu_s = time.perf_counter() - t
-        out["cpu_baseline"] = {"value": tokens / cpu_s, "unit": "tokens/s", "cores": threads,
+        omp = os.environ.get("OMP_NUM_THREADS")
+        threads = int(omp or 0) or (os.cpu_count() or 1)
+
+        def oracle_run(idx, nthreads):
+            wi = wl.WORKLOADS[idx]
+            ii = inp if idx == FWD_INDEX else wl.workload_inputs(idx)
+            io = ii["io"]
+            t = time.perf_counter()
+            if wi["name"] == "decode":
+                oracle.ssd_decode(ii["state"], wl.as_f64(ii["x"], io), ii["dt"], ii["A"], wl.as_f64(ii["B"], io),
+                                  wl.as_f64(ii["C"], io), ii["D"], nthreads=nthreads)
+                ntok = wi["batch"]
+            else:
+                oracle.ssd_fwd(wl.as_f64(ii["x"], io), ii["dt"], ii["A"], wl.as_f64(ii["B"], io),
+                               wl.as_f64(ii["C"], io), ii["D"], init_state=ii.get("init_state"),
+                               cu_seqlens=ii.get("cu_seqlens"), nthreads=nthreads)
+                ntok = ii["x"].shape[0] * ii["x"].shape[1]
+            return ntok, time.perf_counter() - t
+
+        ntok, cpu_s = oracle_run(FWD_INDEX, threads)
+        one_core = {}
+        for idx in (0, 1, 4):      # median of three single-thread runs
+            runs = [oracle_run(idx, 1) for _ in range(3)]
+            med = sorted(r[1] for r in runs)[1]
+            one_core[wl.WORKLOADS[idx]["name"]] = {"tokens_per_s": runs[0][0] / med, "s": med}
+        n3, s3 = oracle_run(3, threads)
+        out["cpu_baseline"] = {"value": ntok / cpu_s, "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
-                               "sample": "the whole workload (4 x 8192 tokens, 80 heads), fp64 "
-                                         f"sequential recurrence, {cpu_s:.1f} s"}
+                               "sample": "the whole 2.7B-layer workload (4 x 8192 tokens, 80 heads), fp64 "
+                                         f"sequential recurrence, one run, {cpu_s:.2f} s",
+                               "cpu_model": cpu_model(), "omp_num_threads": omp, "logical_cpus": os.cpu_count(),
+                               "varlen_packed_all_cores": {"tokens_per_s": n3 / s3, "s": s3},
+                               "one_core": one_core}
     print(json.dumps(out))
 
 
