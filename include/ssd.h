@@ -160,7 +160,9 @@ size_t ssd_chunk_scan_fwd_workspace_size(const ssd_dims_t *dims, int32_t chunk_l
  * 256 and headdim >= 32; fp32: headdim >= 64 with chunk_len 256, and some
  * larger shapes at 128), the kernel runs the largest shorter chunk that fits
  * (at least 64 tokens): chunking only orders the evaluation, so the result is
- * the same up to rounding.  Other sizes return SSD_ERR_UNSUPPORTED.
+ * the same up to rounding.  Other sizes return SSD_ERR_UNSUPPORTED; so
+ * that one chunk of x spans less than 2^30 bytes, nheads * headdim must stay
+ * below 2^20 (else SSD_ERR_SHAPE).
  * x, y, B, C, dt, D and the states must be 16-byte aligned.
  */
 ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, ssd_dtype_t io_dtype,

@@ -566,6 +566,9 @@ ssd_status_t fwd_shape_check(const ssd_dims_t *dims, int32_t chunk_len, ssd_dtyp
     // sizes must stay within the kernels' 32-bit schedule fields
     const long long tokens = (long long)d.batch * d.seqlen;
     if (tokens > INT_MAX / 2) return SSD_ERR_SHAPE;
+    // one chunk of x (or y) rows, all heads, must span less than 2^30 bytes:
+    // the kernel addresses it through a buffer with 30-bit offsets
+    if ((long long)d.nheads * d.headdim * 256 * 4 >= (1LL << 30)) return SSD_ERR_SHAPE;
     return SSD_OK;
 }
 

@@ -11,6 +11,7 @@
 //   H_{c+1} = exp(s_{q-1}) H_c + S_c                     (inter-chunk recurrence)
 //   Y_off   = diag(exp(s_i)) C H_c^T
 //   y       = Y_diag + Y_off + D_h x
+// (D_h x is formed inside Y_diag: D_h is added to the diagonal of the mask.)
 //
 // Decay by blocks.  The chunk is cut into blocks of 64 tokens; e_b is the
 // cumulative sum at the last token of block b.  Each head's x is staged twice
@@ -123,7 +124,8 @@ struct FwdShape {
     static constexpr int PTW = (PT + WP - 1) / WP;   // head-dim tiles per wave
     static constexpr int E = (int)sizeof(IO);
     static constexpr int FRAG_REGS = 8 * E / 4;  // registers per MFMA operand fragment
-    static constexpr int PAD = 16 / E;           // 16 bytes of padding per LDS row
+    // bf16 tiles are unpadded and swizzled (lds_off); fp32 rows carry 16 bytes of padding
+    static constexpr int PAD = E == 2 ? 0 : 16 / E;
     static constexpr int SB = NP + PAD;          // row stride of the B chunk
     static constexpr int SX = Q + PAD;           // row stride of the x^T tiles
     static constexpr int SH = NP + PAD;          // row stride of the incoming state
@@ -164,6 +166,7 @@ struct FwdShape {
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // K-slot order.  Every contraction over chunk tokens uses the same slot
 // order: within a 32-token K step, slot e (0..7) of lane group lg holds token
@@ -176,20 +179,85 @@ __device__ __forceinline__ int xpos(int j) {
     return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
 }
 
+// Element offset of (row, col) in an LDS tile of COLS columns.  bf16 tiles
+// are stored unpadded, with the 16-byte chunk index of each element (col / 8)
+// XORed with the low bits of its row.  A fragment read (16 rows, 16 bytes per
+// lane, the four lane groups at four consecutive chunks) then hands each run
+// of 8 lanes one half of the 64 banks, the other half going to the run it is
+// served with, where a plain row-major layout put two lanes of such a pair on
+// the same banks.  fp32 tiles keep 16 bytes of padding per row instead.  COLS
+// is a power of two of at least 32 in every built shape, so the XOR stays
+// inside the row, and a 4- or 8-element group at a multiple of its size keeps
+// its elements together and in order.
+template <typename IO, int COLS>
+__device__ __forceinline__ int lds_off(int row, int col) {
+    if constexpr (sizeof(IO) == 2) {
+        static_assert((COLS & (COLS - 1)) == 0 && COLS >= 32, "swizzled rows need a power-of-two width");
+        constexpr int CH = COLS / 8;
+        constexpr int MASK = (CH < 16 ? CH : 16) - 1;
+        return row * COLS + (col ^ ((row & MASK) << 3));
+    } else {
+        return row * (COLS + 16 / (int)sizeof(IO)) + col;
+    }
+}
+
+// Buffer resource over `bytes` bytes at `base`: reads past the end return 0
+// and writes past it are dropped (0 bytes: every access is a no-op).  The
+// head loop makes its global accesses through these, with out-of-range
+// offsets instead of branches, so that every path issues the same vector
+// memory operations: the compiler then knows how many follow each load and
+// waits for exactly the ones a use needs (operations issued under a branch
+// make it wait for whatever might have been issued).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+constexpr int kPastEnd = 0x40000000;   // a byte offset beyond every buffer of the kernel
+
+// s_waitcnt operand that waits until at most n vector memory operations are
+// outstanding (and for nothing else): vmcnt in bits 3:0 and 15:14, expcnt (7)
+// and lgkmcnt (15) at their no-wait maxima.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <typename IO>
+__device__ __forceinline__ typename Io<IO>::Frag buf_load_frag(__amdgpu_buffer_rsrc_t r, int off) {
+    typedef typename Io<IO>::Frag Frag;
+    if constexpr (sizeof(IO) == 2) {
+        return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    } else {
+        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+        return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+template <typename IO>
+__device__ __forceinline__ void buf_store_half(typename Io<IO>::Half v, __amdgpu_buffer_rsrc_t r, int off) {
+    if constexpr (sizeof(IO) == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
+    }
+}
+
+template <int AUX = 0>
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
+}
+
 // Unscaled B^T fragment in the K-slot order above: lane holds
 // B[k0 + 16 * (e / 4) + 4 * lg + e % 4][n0 + li], e = 0..7.
-template <typename IO, int SB>
+template <typename IO, int NP>
 __device__ __forceinline__ typename Io<IO>::Frag load_bt_frag(const IO *sB, int k0, int n0, int li, int lg) {
     typename Io<IO>::Frag f;
     if constexpr (sizeof(IO) == 2) {
         const int row = k0 + 4 * lg + (li >> 2);
         const int col = n0 + 4 * (li & 3);
-        const bf16x4 lo = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + row * SB + col));
-        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + (row + 16) * SB + col));
+        const bf16x4 lo = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + lds_off<IO, NP>(row, col)));
+        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const bf16 *>(sB + lds_off<IO, NP>(row + 16, col)));
         f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = sB[(k0 + 16 * (e >> 2) + 4 * lg + (e & 3)) * SB + n0 + li];
+        for (int e = 0; e < 8; ++e) f[e] = sB[lds_off<IO, NP>(k0 + 16 * (e >> 2) + 4 * lg + (e & 3), n0 + li)];
     }
     return f;
 }
@@ -205,9 +273,13 @@ struct Prefetch {
     static constexpr int NUNIT = (Q / 4) * PB;
     static constexpr int NU = (NUNIT + S::kThreads - 1) / S::kThreads;
     static constexpr int R = Q / 64;
+    // vector memory operations issued by load()
+    static constexpr int kLoads = NU * 4 * (sizeof(IO) == 2 ? 1 : 2) + R + 3;
+    static_assert(kLoads < 64, "vmcnt holds at most 63");
     Frag x[NU][4];
     float dt[R];
     float a;   // A[h] (wave 0)
+    float d;   // D[h], 0 without D (wave 0)
     float braw; // dt_bias[h] (A[h] when there is no bias; not used then)
 
     // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  Sixteen
@@ -216,9 +288,14 @@ struct Prefetch {
     static __device__ __forceinline__ int unit_t4(int u) { return (u & 15) + 16 * (u / (16 * PB)); }
     static __device__ __forceinline__ int unit_p0(int u) { return ((u >> 4) % PB) * 8; }
 
-    __device__ __forceinline__ void load(const FwdParams &prm, long long tok0, int q, int h, int tid) {
+    // Head h's x chunk (every wave) and its dt, A, D and dt_bias (wave 0;
+    // empty buffers elsewhere); tokens past the chunk read 0.  `live` false
+    // (no such head) empties every buffer, so the same loads are issued.
+    __device__ __forceinline__ void load(const FwdParams &prm, long long tok0, int q, int h, int tid, int wave,
+                                         bool live) {
         const int xs = prm.H * P;
         const IO *xg = reinterpret_cast<const IO *>(prm.x) + tok0 * xs + h * P;
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xg, live ? q * xs * S::E : 0);
 #pragma unroll
         for (int k = 0; k < NU; ++k) {
             const int u = tid + k * S::kThreads;
@@ -226,24 +303,24 @@ struct Prefetch {
             const int p0 = unit_p0(u);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int i = 4 * t4 + t;
-                x[k][t] = zero_frag<Frag>();
-                if (u < NUNIT && i < q) x[k][t] = *reinterpret_cast<const Frag *>(xg + i * xs + p0);
+                const int i = 4 * t4 + t;   // i >= q lies past the buffer's end
+                const bool uok = NUNIT % S::kThreads == 0 || u < NUNIT;
+                x[k][t] = buf_load_frag<IO>(rx, uok ? (i * xs + p0) * S::E : kPastEnd);
             }
         }
-        if (tid < 64) {
+        const int hm = h / prm.hsub, Hm = prm.H / prm.hsub;
+        const bool mine = live && wave == 0;
+        const __amdgpu_buffer_rsrc_t rdt = buf_rsrc(prm.dt + tok0 * Hm + hm, mine ? ((q - 1) * Hm + 1) * 4 : 0);
+        const int lane = tid & 63;
 #pragma unroll
-            for (int k = 0; k < R; ++k) {
-                const int i = tid * R + k;
-                dt[k] = (i < q) ? prm.dt[(tok0 + i) * (prm.H / prm.hsub) + h / prm.hsub] : 0.f;
-            }
-            a = prm.A[h / prm.hsub];
-            braw = (prm.dtp.bias ? prm.dtp.bias : prm.A)[h / prm.hsub];   // branch-free
-        }
+        for (int k = 0; k < R; ++k) dt[k] = buf_load_f32(rdt, (lane * R + k) * Hm * 4);
+        a = buf_load_f32(buf_rsrc(prm.A + hm, mine ? 4 : 0), 0);
+        d = buf_load_f32(buf_rsrc(prm.D ? prm.D + hm : prm.A, mine && prm.D ? 4 : 0), 0);
+        braw = buf_load_f32(buf_rsrc((prm.dtp.bias ? prm.dtp.bias : prm.A) + hm, mine ? 4 : 0), 0);
     }
 
     // wave 0: dt (lane holds tokens R*lane .. R*lane+R-1, preprocessed when
-    // asked; tokens past the chunk stay 0) and A into LDS
+    // asked; tokens past the chunk stay 0), A and D into LDS
     __device__ __forceinline__ void stage_dt(float *sStage, int lane, int q, const DtProc &dtp) const {
 #pragma unroll
         for (int k = 0; k < R; ++k) {
@@ -251,7 +328,10 @@ struct Prefetch {
             if (dtp.on && lane * R + k < q) v = dtp.apply(v, dtp.bias ? braw : 0.f);
             sStage[lane * R + k] = v;
         }
-        if (lane == 0) sStage[Q] = a;
+        if (lane == 0) {
+            sStage[Q] = a;
+            sStage[Q + 1] = d;
+        }
     }
 
     // x^T[p][i .. i+3] from 4 tokens of one channel, as is into sX and times
@@ -278,8 +358,8 @@ struct Prefetch {
                         v[t] = x[k][t][e];
                         w[t] = from_f32<IO>(to_f32(x[k][t][e]) * fac[t]);
                     }
-                    *reinterpret_cast<Half *>(sX + (p0 + e) * S::SX + pos) = v;
-                    *reinterpret_cast<Half *>(sXh + (p0 + e) * S::SX + pos) = w;
+                    *reinterpret_cast<Half *>(sX + lds_off<IO, Q>(p0 + e, pos)) = v;
+                    *reinterpret_cast<Half *>(sXh + lds_off<IO, Q>(p0 + e, pos)) = w;
                 }
             }
         }
@@ -351,7 +431,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
 
         // ---- first head's x and dt, then the B chunk (row layout) into LDS ----
         Prefetch<IO, P, N, Q> pf;
-        pf.load(prm, tok0, q, h_begin, tid);
+        pf.load(prm, tok0, q, h_begin, tid, wave, true);
         {
             constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
             constexpr int VN = N * S::E / 16;        // vectors that hold data
@@ -370,7 +450,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 const int u = tid + k * S::kThreads;
                 const int j = u / VPR;
                 const int c = u - j * VPR;
-                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sB + j * S::SB + c * (16 / S::E)) = bv[k];
+                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sB + lds_off<IO, S::NP>(j, c * (16 / S::E))) = bv[k];
             }
         }
 
@@ -409,7 +489,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 f32x4 acc = zero4();
     #pragma unroll
                 for (int ks = 0; ks < S::NK; ++ks) {
-                    const Frag bfr = *reinterpret_cast<const Frag *>(sB + (16 * jt + li) * S::SB + ks * 32 + 8 * lg);
+                    const Frag bfr = *reinterpret_cast<const Frag *>(sB + lds_off<IO, S::NP>(16 * jt + li, ks * 32 + 8 * lg));
                     acc = Io<IO>::mfma(acc, bfr, useA ? cga[ks] : cgb[ks]);
                 }
     #pragma unroll
@@ -428,7 +508,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     #pragma unroll
                 for (int ks = 0; ks < S::QK; ++ks) {
                     btr[a][ks] = zero_frag<Frag>();
-                    if (wp < S::PT && nt < S::NT) btr[a][ks] = load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg);
+                    if (wp < S::PT && nt < S::NT) btr[a][ks] = load_bt_frag<IO, S::NP>(sB, ks * 32, nt * 16, li, lg);
                 }
             }
         }
@@ -447,7 +527,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 const int c = u - j * VPR;
                 i32x4 v = i32x4{0, 0, 0, 0};
                 if (u < Q * VPR && j < q && c < VN) v = *reinterpret_cast<const i32x4 *>(Cg + j * bs + c * (16 / S::E));
-                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sC + j * S::SB + c * (16 / S::E)) = v;
+                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sC + lds_off<IO, S::NP>(j, c * (16 / S::E))) = v;
             }
             // (read only after the first head's staging barrier)
         } else if constexpr (S::kAliasB) {
@@ -472,8 +552,9 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         // own decay block: lane holds M[i_row][j], j = 32 ks + 16 half + 4 lg + r.
         // Below the diagonal 16-tile: G * exp(s_i - s_r) * exp(s_r - s_j) dt_j
         // (both factors <= 1, r the last token of j's 16-tile); on it the exact
-        // exp(s_i - s_j) with a causal select.
-        auto mask_frag = [&](auto from_a, int I, int ks, float s2_i, const float (&sref)[S::QT]) {
+        // exp(s_i - s_j) with a causal select, and the skip coefficient D added
+        // on the diagonal itself (y_i gains D x_i from the same product).
+        auto mask_frag = [&](auto from_a, int I, int ks, float s2_i, const float (&sref)[S::QT], float dh) {
             constexpr bool fromA = decltype(from_a)::value;
             const int i_row = 16 * I + li;
             Frag m;
@@ -495,7 +576,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     const f32x4 dtj = *reinterpret_cast<const f32x4 *>(vDt + j0);
     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r];
+                        const float v = gv[r] * exp2f_fast(s2_i - s2j[r]) * dtj[r] + (j0 + r == i_row ? dh : 0.f);
                         m[4 * half + r] = from_f32<IO>((j0 + r <= i_row) ? v : 0.f);
                     }
                 } else {
@@ -504,25 +585,6 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 }
             }
             return m;
-        };
-        // x^T[pt*16 + 4 lg + r][16 I + li], r = 0..3, for the skip term: one
-        // transposing read per head-dim tile (lane 4e + c of a 16-lane group
-        // points at row pt*16 + 4 lg + e, tokens 16 I + 4c .. 4c + 3, which sit
-        // at consecutive positions of the K-slot order).
-        auto x_rows = [&](int I, int pt) -> f32x4 {
-            f32x4 v;
-            if constexpr (sizeof(IO) == 2) {
-                const int e = li >> 2, c = li & 3;
-                const bf16x4 t = lds_read_tr16(reinterpret_cast<const bf16 *>(
-                    sX + (pt * 16 + 4 * lg + e) * S::SX + 32 * (I >> 1) + 8 * c + 4 * (I & 1)));
-    #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = to_f32(t[r]);
-            } else {
-                const int xp = xpos(16 * I + li);
-    #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = sX[(pt * 16 + 4 * lg + r) * S::SX + xp];
-            }
-            return v;
         };
         // Runs f with this wave's index as a compile-time constant, so that the
         // phases below are unrolled without any branch on the wave's row tiles.
@@ -563,6 +625,12 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         };
 
         int *sReady = sTicket + 1;
+        // Cache policy of the hand-off: the stores are ordinary, so H_{c+1}
+        // stays in this XCD's L2 (write-back); the loads (state and counter)
+        // are device scope (sc1), which skips the compute unit's L1 (it may
+        // hold an older version of these in-place lines) and is served by the
+        // same L2.
+        constexpr int kStateLoad = 16;   // sc1
 
     #pragma unroll 1
         for (int h = h_begin; h < h_end; ++h) {
@@ -583,18 +651,20 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             const int unit = seq * H + h;
 
             // ---- (1) in-chunk cumulative sum, per-token vectors, x^T and xh^T ----
+            float Dh;   // skip coefficient D[h] (0 without D)
             {
                 // one early look at the predecessor's flag (the state loads can
                 // then be issued before the compute phase)
                 // (compared only after the scan, so that the scan does not wait for it)
-                int flagv = INT_MAX;
-                if (wave == 0 && lane == 0 && cloc > 0)
-                    flagv = __hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // (wave 0 reads it; an empty buffer elsewhere and for the first chunk)
+                int flagv = __builtin_bit_cast(
+                    int, buf_load_f32<kStateLoad>(buf_rsrc(prm.flags + unit, wave == 0 && cloc > 0 ? 4 : 0), 0));
                 // Every wave scans the whole chunk (R tokens per lane, from the
                 // staged dt) and writes the per-token vectors of its own Q/8
                 // tokens (lanes 8 wave .. 8 wave + 7).
                 constexpr int R = Q / 64;
                 const float Ah = sStage[Q];
+                Dh = sStage[Q + 1];
                 float dtv[R];
     #pragma unroll
                 for (int k = 0; k < R; ++k) dtv[k] = sStage[lane * R + k];
@@ -629,37 +699,32 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 }
                 pf.stage(sX, sXh, tid, [&](int k, int src) { return __shfl(fh[k], src, 64); });
                 asm volatile("" : "+v"(flagv));   // keeps the comparison (and its wait) here
-                if (wave == 0 && lane == 0) *sReady = flagv >= S::kWaves * cloc;
+                if (wave == 0 && lane == 0) *sReady = cloc == 0 || flagv >= S::kWaves * cloc;
             }
             __syncthreads();
             const float s2_last = vS2[Q - 1];
             const bool early = *sReady != 0;
 
-            // incoming boundary state, issued now
-            // when the predecessor had already published, else after the wait below
+            // Incoming boundary state: issued here, ahead of the compute phase,
+            // when the predecessor had already published (its latency then
+            // hides behind the compute phase), else after the wait below.
             const float *hin = (cloc == 0) ? (prm.init_state ? prm.init_state + (long long)unit * P * N : nullptr)
                                            : prm.state + (long long)unit * P * N;
             float *hout = prm.state + (long long)unit * P * N;
-            // Cache policy of the hand-off: the stores are ordinary, so H_{c+1}
-            // stays in this XCD's L2 (write-back); the loads are device scope
-            // (sc1), which skips the compute unit's L1 (it may hold an older
-            // version of these in-place lines) and is served by the same L2.
-            constexpr int kStateLoad = 16;   // sc1
             f32x4 hv[S::NTW][S::PTW];
-            auto load_state = [&]() {
-                const __amdgpu_buffer_rsrc_t rin =
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(hin), 0, hin ? P * N * 4 : 0, 0x00020000);
+            auto load_state = [&](bool on) {   // (off: an empty buffer, the same loads)
+                const __amdgpu_buffer_rsrc_t rin = buf_rsrc(hin, hin && on ? P * N * 4 : 0);
     #pragma unroll
                 for (int a = 0; a < S::NTW; ++a)
     #pragma unroll
                     for (int b = 0; b < S::PTW; ++b) {
                         const int nt = wn + a * S::WN, pt = wp + b * S::WP;
-                        hv[a][b] = zero4();
-                        if (wp < S::PT && nt < S::NT && pt < S::PT && hin)
-                            hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                rin, ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4, 0, kStateLoad));
+                        const bool ok = wp < S::PT && nt < S::NT && pt < S::PT;
+                        hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                            rin, ok ? ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4 : kPastEnd, 0, kStateLoad));
                     }
             };
+            load_state(early);
 
             // ---- (2) compute: chunk state and both tiles' diagonal blocks ----
             // One pass over the K steps.  Each step reads the xh^T fragments of
@@ -705,12 +770,12 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 auto load_step = [&](int ks, Frag (&xo)[S::PT], Frag (&bo)[S::NTW]) {
     #pragma unroll
                     for (int pt = 0; pt < S::PT; ++pt)
-                        xo[pt] = *reinterpret_cast<const Frag *>(sXh + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                        xo[pt] = *reinterpret_cast<const Frag *>(sXh + lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
     #pragma unroll
                     for (int a = 0; a < S::NTW; ++a) {
                         const int nt = WNc + a * S::WN;
                         if constexpr (S::kBtRegs) bo[a] = btr[a][ks];
-                        else bo[a] = (HS && nt < S::NT) ? load_bt_frag<IO, S::SB>(sB, ks * 32, nt * 16, li, lg)
+                        else bo[a] = (HS && nt < S::NT) ? load_bt_frag<IO, S::NP>(sB, ks * 32, nt * 16, li, lg)
                                                         : zero_frag<Frag>();
                     }
                 };
@@ -727,8 +792,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     Frag xea[S::PT], xeb[S::PT];
     #pragma unroll
                     for (int pt = 0; pt < S::PT; ++pt) {
-                        if (exA) xea[pt] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
-                        if (exB) xeb[pt] = *reinterpret_cast<const Frag *>(sX + (pt * 16 + li) * S::SX + ks * 32 + 8 * lg);
+                        if (exA) xea[pt] = *reinterpret_cast<const Frag *>(sX + lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
+                        if (exB) xeb[pt] = *reinterpret_cast<const Frag *>(sX + lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
                     }
                     if (ks % S::KPB == 0 && blk > 0) {
                         // block decay exp(e_b - e_{b-1}) on every sum still in its recurrence
@@ -766,12 +831,12 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                         for (int pt = 0; pt < S::PT; ++pt) accYb[pt] = Io<IO>::mfma(accYb[pt], xh[cur][pt], m);
                     }
                     if (exA) {
-                        const Frag m = mask_frag(std::true_type{}, T.IA, ks, s2_ia, sref);
+                        const Frag m = mask_frag(std::true_type{}, T.IA, ks, s2_ia, sref, Dh);
     #pragma unroll
                         for (int pt = 0; pt < S::PT; ++pt) accYa[pt] = Io<IO>::mfma(accYa[pt], xea[pt], m);
                     }
                     if (exB) {
-                        const Frag m = mask_frag(std::false_type{}, T.IB, ks, s2_ib, sref);
+                        const Frag m = mask_frag(std::false_type{}, T.IB, ks, s2_ib, sref, Dh);
     #pragma unroll
                         for (int pt = 0; pt < S::PT; ++pt) accYb[pt] = Io<IO>::mfma(accYb[pt], xeb[pt], m);
                     }
@@ -780,11 +845,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             });
 
             // ---- (3) chain: wait if needed, H_{c+1} = exp(s_last) H_c + S_c, H_c to LDS ----
-            // One thread waits for the predecessor's counter; the incoming state's
-            // loads are then issued before the next head's x and dt prefetch:
-            // loads complete in order, so waiting for the state never waits for
-            // the prefetch.
-            if (early) load_state();
+            // One thread waits for the predecessor's counter, then every wave
+            // loads the incoming state.
             if (!early || S::kAliasH) {
                 if (!early && tid == 0) {
                     int it = 0;
@@ -799,43 +861,47 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 }
                 // (also: with the state tile over xh^T, every wave has left the compute phase)
                 __syncthreads();
-                if (!early) load_state();
+                if (!early) load_state(true);
             }
-            if (h + 1 < h_end) pf.load(prm, tok0, q, h + 1, tid);
             Frag cfa[S::kCInLds ? 1 : S::NK], cfb[S::kCInLds ? 1 : S::NK];
             if constexpr (!S::kCInLds) {
                 load_c(hasA ? Ia : S::QT, cfa);
                 load_c(hasB ? Ib : S::QT, cfb);
             }
             const float alpha = exp2f_fast(s2_last);
-            const float Dh = prm.D ? prm.D[h / prm.hsub] : 0.f;   // needed only by the epilogue
-            if (wp < S::PT) {
-                const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(hout, 0, P * N * 4, 0x00020000);
+            {
+                const __amdgpu_buffer_rsrc_t rout = buf_rsrc(hout, P * N * 4);
     #pragma unroll
                 for (int a = 0; a < S::NTW; ++a)
     #pragma unroll
                     for (int b = 0; b < S::PTW; ++b) {
                         const int nt = wn + a * S::WN, pt = wp + b * S::WP;
-                        if (nt < S::NT && pt < S::PT) {
-                            const int p = pt * 16 + li;
-                            const int n0 = nt * 16 + 4 * lg;
-                            f32x4 o;
-                            Half hb;
+                        const bool ok = wp < S::PT && nt < S::NT && pt < S::PT;
+                        const int p = pt * 16 + li;
+                        const int n0 = nt * 16 + 4 * lg;
+                        f32x4 o;
+                        Half hb;
     #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                o[r] = alpha * hv[a][b][r] + accS[a][b][r];
-                                hb[r] = from_f32<IO>(hv[a][b][r]);
-                            }
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout, (p * N + n0) * 4,
-                                                                   0, 0);
-                            *reinterpret_cast<Half *>(sH + p * S::SH + n0) = hb;
+                        for (int r = 0; r < 4; ++r) {
+                            o[r] = alpha * hv[a][b][r] + accS[a][b][r];
+                            hb[r] = from_f32<IO>(hv[a][b][r]);
                         }
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout,
+                                                               ok ? (p * N + n0) * 4 : kPastEnd, 0, 0);
+                        if (ok) *reinterpret_cast<Half *>(sH + lds_off<IO, S::NP>(p, n0)) = hb;
                     }
             }
+            // The next head's x and dt, issued after the state stores: the
+            // read-out below then waits for the stores alone (vector memory
+            // operations complete in issue order), and the prefetch has until
+            // the next head's staging to arrive.
+            __builtin_amdgcn_sched_barrier(0);
+            pf.load(prm, tok0, q, h + 1, tid, wave, h + 1 < h_end);
+            __builtin_amdgcn_sched_barrier(0);
             if constexpr (S::NP != N) {   // zero K slots past the state dim
                 for (int v = tid; v < P * (S::NP - N); v += S::kThreads) {
                     const int p = v / (S::NP - N);
-                    sH[p * S::SH + N + (v - p * (S::NP - N))] = from_f32<IO>(0.f);
+                    sH[lds_off<IO, S::NP>(p, N + (v - p * (S::NP - N)))] = from_f32<IO>(0.f);
                 }
             }
             __syncthreads();  // H_c is in LDS
@@ -845,7 +911,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             // steps (each H fragment is read once); then each wave publishes its
             // part of H_{c+1} (one increment of the (sequence, head) counter) once
             // its state stores are acknowledged -- a successor waits for all
-            // kWaves increments -- and writes y = Y_diag + exp(s_i) Y_off + D x.
+            // kWaves increments -- and writes y = Y_diag + exp(s_i) Y_off (Y_diag
+            // already holds D x, from the mask's diagonal).
             with_wave([&](auto wc) {
                 constexpr WaveTiles T = tiles_of(wc);
                 f32x4 oa[S::PT], ob[S::PT];
@@ -859,10 +926,10 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 auto load_h = [&](int ks, Frag (&o)[S::PT], Frag &oa_, Frag &ob_) {
     #pragma unroll
                     for (int pt = 0; pt < S::PT; ++pt)
-                        o[pt] = *reinterpret_cast<const Frag *>(sH + (pt * 16 + li) * S::SH + ks * 32 + 8 * lg);
+                        o[pt] = *reinterpret_cast<const Frag *>(sH + lds_off<IO, S::NP>(pt * 16 + li, ks * 32 + 8 * lg));
                     if constexpr (S::kCInLds) {
-                        if (T.HA) oa_ = *reinterpret_cast<const Frag *>(sC + (16 * T.IA + li) * S::SB + ks * 32 + 8 * lg);
-                        if (T.HB) ob_ = *reinterpret_cast<const Frag *>(sC + (16 * T.IB + li) * S::SB + ks * 32 + 8 * lg);
+                        if (T.HA) oa_ = *reinterpret_cast<const Frag *>(sC + lds_off<IO, S::NP>(16 * T.IA + li, ks * 32 + 8 * lg));
+                        if (T.HB) ob_ = *reinterpret_cast<const Frag *>(sC + lds_off<IO, S::NP>(16 * T.IB + li, ks * 32 + 8 * lg));
                     } else {
                         oa_ = cfa[S::kCInLds ? 0 : ks];
                         ob_ = cfb[S::kCInLds ? 0 : ks];
@@ -881,22 +948,22 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_s_waitcnt(0);  // this wave's state stores are acknowledged
-                if (lane == 0) __hip_atomic_fetch_add(prm.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // this wave's state stores are acknowledged: everything but the
+                // prefetch's loads, the last ones issued, has completed
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(Prefetch<IO, P, N, Q>::kLoads));
+                // (lane 0 adds; the other lanes' offsets lie past the counter)
+                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, buf_rsrc(prm.flags + unit, 4), lane == 0 ? 0 : kPastEnd,
+                                                                     0, 0);
+                const __amdgpu_buffer_rsrc_t ry = buf_rsrc(yg, q * xs * S::E);   // rows i >= q lie past its end
                 auto epilogue = [&](int I, const f32x4 (&o)[S::PT], const f32x4 (&accY)[S::PT]) {
                     const int i_row = 16 * I + li;
-                    f32x4 xv[S::PT];
-    #pragma unroll
-                    for (int pt = 0; pt < S::PT; ++pt) xv[pt] = x_rows(I, pt);
                     const float eo = vEo[i_row];
-                    if (i_row < q) {
     #pragma unroll
-                        for (int pt = 0; pt < S::PT; ++pt) {
-                            Half yv;
+                    for (int pt = 0; pt < S::PT; ++pt) {
+                        Half yv;
     #pragma unroll
-                            for (int r = 0; r < 4; ++r) yv[r] = from_f32<IO>(accY[pt][r] + eo * o[pt][r] + Dh * xv[pt][r]);
-                            *reinterpret_cast<Half *>(yg + i_row * xs + pt * 16 + 4 * lg) = yv;
-                        }
+                        for (int r = 0; r < 4; ++r) yv[r] = from_f32<IO>(accY[pt][r] + eo * o[pt][r]);
+                        buf_store_half<IO>(yv, ry, (i_row * xs + pt * 16 + 4 * lg) * S::E);
                     }
                 };
                 if (T.HA) epilogue(T.IA, oa, accYa);
