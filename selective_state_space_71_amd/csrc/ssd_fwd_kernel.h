@@ -161,6 +161,9 @@ struct FwdShape {
     static constexpr int kLds = kAliasB ? kLdsVec + cmax(kHeadBytes, kLdsB) : kLdsVec + kHeadBytes + kLdsB;
     // C rows for the read-out in the B chunk's LDS (dead once B^T is in registers)
     static constexpr bool kCInLds = kCInLdsWanted && !kAliasB;
+    // y rows leave through LDS (xh^T's space, of exactly the y tile's size) when
+    // they are 128 bytes (bf16, P = 64) and that space is not the state tile's
+    static constexpr bool kYViaLds = E == 2 && P == 64 && !kAliasH;
     static constexpr bool kFits = (kFitSep || kFitAliasH || kFitAliasB || kFitAliasHB) && QT <= 2 * kWaves &&
                                   Q % BLK == 0;
 };
@@ -244,6 +247,28 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, int off)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
 }
 
+// Element offset of (row = channel, col = K-slot position) in the x^T and xh^T
+// tiles: lds_off's swizzle with bits 4-5 of the row also XORed into chunk bits
+// 1-2.  A fragment read (rows 16 pt .. 16 pt + 15) sees lds_off's pattern
+// XORed with a constant; the staging writes (eight channel blocks of one token
+// group per 8-lane run, see Prefetch) then land on distinct banks as well.
+template <typename IO, int COLS>
+__device__ __forceinline__ int x_lds_off(int row, int col) {
+    if constexpr (sizeof(IO) == 2) {
+        constexpr int CH = COLS / 8;
+        constexpr int MASK = (CH < 16 ? CH : 16) - 1;
+        return row * COLS + (col ^ (((row ^ ((row >> 4) << 1)) & MASK) << 3));
+    } else {
+        return lds_off<IO, COLS>(row, col);
+    }
+}
+
+// Element offset of (row, col) in the y tile staged for the output stores:
+// rows of 64 bf16 (128 bytes), the 16-byte chunk index XORed with bits 1..3 of
+// the row, so that sixteen lanes writing 8 bytes at one column of sixteen rows,
+// and eight lanes reading one row's eight chunks, spread over the banks.
+__device__ __forceinline__ int y_lds_off(int row, int col) { return row * 64 + (col ^ (((row >> 1) & 7) << 3)); }
+
 // Unscaled B^T fragment in the K-slot order above: lane holds
 // B[k0 + 16 * (e / 4) + 4 * lg + e % 4][n0 + li], e = 0..7.
 template <typename IO, int NP>
@@ -282,11 +307,21 @@ struct Prefetch {
     float d;   // D[h], 0 without D (wave 0)
     float braw; // dt_bias[h] (A[h] when there is no bias; not used then)
 
-    // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  Sixteen
-    // consecutive units take sixteen consecutive token groups of one channel
-    // block, so the transposing LDS writes of 16 lanes hit distinct banks.
-    static __device__ __forceinline__ int unit_t4(int u) { return (u & 15) + 16 * (u / (16 * PB)); }
-    static __device__ __forceinline__ int unit_p0(int u) { return ((u >> 4) % PB) * 8; }
+    // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  With 64
+    // channels (eight blocks), the eight lanes of a run take the eight blocks
+    // of one token group, so a wave's load instruction reads whole 128-byte
+    // rows of x; lane bit 3 and lane bits 4-5 pick the token group, which with
+    // x_lds_off's swizzle keeps the 8-byte staging writes of 32 lanes on
+    // distinct banks.  Other widths: sixteen consecutive units take sixteen
+    // consecutive token groups of one channel block.
+    static __device__ __forceinline__ int unit_t4(int u) {
+        if constexpr (PB == 8) return 8 * (u >> 6) + 4 * ((u >> 3) & 1) + ((u >> 4) & 3);
+        else return (u & 15) + 16 * (u / (16 * PB));
+    }
+    static __device__ __forceinline__ int unit_p0(int u) {
+        if constexpr (PB == 8) return 8 * (u & 7);
+        else return ((u >> 4) % PB) * 8;
+    }
 
     // Head h's x chunk (every wave) and its dt, A, D and dt_bias (wave 0;
     // empty buffers elsewhere); tokens past the chunk read 0.  `live` false
@@ -358,8 +393,8 @@ struct Prefetch {
                         v[t] = x[k][t][e];
                         w[t] = from_f32<IO>(to_f32(x[k][t][e]) * fac[t]);
                     }
-                    *reinterpret_cast<Half *>(sX + lds_off<IO, Q>(p0 + e, pos)) = v;
-                    *reinterpret_cast<Half *>(sXh + lds_off<IO, Q>(p0 + e, pos)) = w;
+                    *reinterpret_cast<Half *>(sX + x_lds_off<IO, Q>(p0 + e, pos)) = v;
+                    *reinterpret_cast<Half *>(sXh + x_lds_off<IO, Q>(p0 + e, pos)) = w;
                 }
             }
         }
@@ -770,7 +805,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 auto load_step = [&](int ks, Frag (&xo)[S::PT], Frag (&bo)[S::NTW]) {
     #pragma unroll
                     for (int pt = 0; pt < S::PT; ++pt)
-                        xo[pt] = *reinterpret_cast<const Frag *>(sXh + lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
+                        xo[pt] = *reinterpret_cast<const Frag *>(sXh + x_lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
     #pragma unroll
                     for (int a = 0; a < S::NTW; ++a) {
                         const int nt = WNc + a * S::WN;
@@ -792,8 +827,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     Frag xea[S::PT], xeb[S::PT];
     #pragma unroll
                     for (int pt = 0; pt < S::PT; ++pt) {
-                        if (exA) xea[pt] = *reinterpret_cast<const Frag *>(sX + lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
-                        if (exB) xeb[pt] = *reinterpret_cast<const Frag *>(sX + lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
+                        if (exA) xea[pt] = *reinterpret_cast<const Frag *>(sX + x_lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
+                        if (exB) xeb[pt] = *reinterpret_cast<const Frag *>(sX + x_lds_off<IO, Q>(pt * 16 + li, ks * 32 + 8 * lg));
                     }
                     if (ks % S::KPB == 0 && blk > 0) {
                         // block decay exp(e_b - e_{b-1}) on every sum still in its recurrence
@@ -955,19 +990,51 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, buf_rsrc(prm.flags + unit, 4), lane == 0 ? 0 : kPastEnd,
                                                                      0, 0);
                 const __amdgpu_buffer_rsrc_t ry = buf_rsrc(yg, q * xs * S::E);   // rows i >= q lie past its end
-                auto epilogue = [&](int I, const f32x4 (&o)[S::PT], const f32x4 (&accY)[S::PT]) {
-                    const int i_row = 16 * I + li;
-                    const float eo = vEo[i_row];
+                if constexpr (S::kYViaLds) {
+                    // The wave's rows go through LDS (xh^T's space, dead since
+                    // the compute phase) and leave as whole 128-byte rows, one
+                    // 16-byte store per lane, rather than as 32-byte pieces of
+                    // four stores.  Only this wave touches these rows.
+                    IO *sY = sXh;
+                    auto y_to_lds = [&](int I, const f32x4 (&o)[S::PT], const f32x4 (&accY)[S::PT]) {
+                        const int i_row = 16 * I + li;
+                        const float eo = vEo[i_row];
     #pragma unroll
-                    for (int pt = 0; pt < S::PT; ++pt) {
-                        Half yv;
+                        for (int pt = 0; pt < S::PT; ++pt) {
+                            Half yv;
     #pragma unroll
-                        for (int r = 0; r < 4; ++r) yv[r] = from_f32<IO>(accY[pt][r] + eo * o[pt][r]);
-                        buf_store_half<IO>(yv, ry, (i_row * xs + pt * 16 + 4 * lg) * S::E);
-                    }
-                };
-                if (T.HA) epilogue(T.IA, oa, accYa);
-                if (T.HB) epilogue(T.IB, ob, accYb);
+                            for (int r = 0; r < 4; ++r) yv[r] = from_f32<IO>(accY[pt][r] + eo * o[pt][r]);
+                            *reinterpret_cast<Half *>(sY + y_lds_off(i_row, pt * 16 + 4 * lg)) = yv;
+                        }
+                    };
+                    auto y_rows = [&](int I) {
+    #pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const int row = 16 * I + 8 * k + (lane >> 3);
+                            const int col = 8 * (lane & 7);
+                            const i32x4 v = *reinterpret_cast<const i32x4 *>(sY + y_lds_off(row, col));
+                            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (row * xs + col) * S::E, 0, 0);
+                        }
+                    };
+                    if (T.HA) y_to_lds(T.IA, oa, accYa);
+                    if (T.HB) y_to_lds(T.IB, ob, accYb);
+                    if (T.HA) y_rows(T.IA);
+                    if (T.HB) y_rows(T.IB);
+                } else {
+                    auto epilogue = [&](int I, const f32x4 (&o)[S::PT], const f32x4 (&accY)[S::PT]) {
+                        const int i_row = 16 * I + li;
+                        const float eo = vEo[i_row];
+    #pragma unroll
+                        for (int pt = 0; pt < S::PT; ++pt) {
+                            Half yv;
+    #pragma unroll
+                            for (int r = 0; r < 4; ++r) yv[r] = from_f32<IO>(accY[pt][r] + eo * o[pt][r]);
+                            buf_store_half<IO>(yv, ry, (i_row * xs + pt * 16 + 4 * lg) * S::E);
+                        }
+                    };
+                    if (T.HA) epilogue(T.IA, oa, accYa);
+                    if (T.HB) epilogue(T.IB, ob, accYb);
+                }
             });
             if (wave == 0 && h + 1 < h_end) pf.stage_dt(sStage, lane, q, prm.dtp);   // the next head's dt and A
             __syncthreads();  // every wave is done with this head's LDS tiles
