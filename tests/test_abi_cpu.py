@@ -95,6 +95,7 @@ def test_workspace_size_query(lib):
     (dict(dims=_dims(headdim=48)), 4),
     (dict(dims=_dims(dstate=48)), 4),                            # state dim not built
     (dict(dims=_dims(headdim=256)), 4),                          # head dim not built
+    (dict(dims=_dims(nheads=1 << 14, ngroups=1)), 2),            # one chunk of x would span 2^30 bytes
     (dict(x=None), 1),
     (dict(A=None), 1),
     (dict(ws=None), 7),
