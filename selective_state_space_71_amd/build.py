@@ -20,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
+# race-widening debug build (SSD_RACE_WIDEN=1), used by tests/test_gpu_race.py
+RACE_LIB = os.path.join(PKG, "libssd_racewiden.so")
 SOURCES = ["ssd_api.hip", "ssd_fwd_bf16.hip", "ssd_fwd_f32.hip"]
 ARCH = "gfx950"
 
@@ -41,31 +43,41 @@ def common_flags():
     ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, race_widen: bool = False) -> str:
+    sub = os.path.join(BUILD, "race") if race_widen else BUILD
+    obj = os.path.join(sub, os.path.splitext(src)[0] + ".o")
+    extra = ["-DSSD_RACE_WIDEN=1"] if race_widen else []
+    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr[-6000:]}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every translation unit and link libssd.so.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, race_widen: bool = False) -> str:
+    """Compile every translation unit and link libssd.so (with race_widen:
+    the debug build libssd_racewiden.so).  Always rebuilds."""
+    os.makedirs(os.path.join(BUILD, "race") if race_widen else BUILD, exist_ok=True)
     t0 = time.time()
+    lib_path = RACE_LIB if race_widen else LIB
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, race_widen), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr[-6000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"[ssd build] {LIB} ({time.time() - t0:.1f}s)", file=sys.stderr)
-    return LIB
+        print(f"[ssd build] {lib_path} ({time.time() - t0:.1f}s)", file=sys.stderr)
+    return lib_path
+
+
+def build_all(verbose: bool = True) -> None:
+    """The library and its race-widening debug build."""
+    build(verbose)
+    build(verbose, race_widen=True)
 
 
 if __name__ == "__main__":
-    build()
+    build_all()

@@ -64,7 +64,28 @@
 
 #include "ssd_device.h"
 
+// Debug build switch (0 in the library; 1 in the race-widening build).
+#ifndef SSD_RACE_WIDEN
+#define SSD_RACE_WIDEN 0
+#endif
+
 namespace ssd {
+
+// Race-widening debug build: before storing its part of H_{c+1}, each
+// producer wave sleeps a time that varies with the unit, the chunk and the
+// wave (0 to 15 x 512 cycles).  The parts of one state then land far apart,
+// so a consumer that read before the counter reached all kWaves increments,
+// or whose loads could be served from a stale copy, would see old values.
+// The arithmetic is unchanged: outputs must stay bitwise equal to the
+// ordinary build's.
+__device__ __forceinline__ void race_widen_delay(int unit, int cloc, int wave) {
+    if constexpr (SSD_RACE_WIDEN != 0) {
+        const int n = (unit * 7 + cloc * 13 + wave * 5) & 15;
+        for (int k = 0; k < n; ++k) __builtin_amdgcn_s_sleep(8);
+    } else {
+        (void)unit, (void)cloc, (void)wave;
+    }
+}
 
 struct FwdParams {
     const void *x;
@@ -904,6 +925,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 load_c(hasB ? Ib : S::QT, cfb);
             }
             const float alpha = exp2f_fast(s2_last);
+            race_widen_delay(unit, cloc, wave);
             {
                 const __amdgpu_buffer_rsrc_t rout = buf_rsrc(hout, P * N * 4);
     #pragma unroll

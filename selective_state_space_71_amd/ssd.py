@@ -21,6 +21,7 @@ Shapes (row-major, contiguous):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -29,6 +30,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssd.so")
+RACE_WIDEN_LIB_PATH = os.path.join(_HERE, "libssd_racewiden.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ssd.h")
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -120,6 +122,20 @@ def load_library(path: str = LIB_PATH):
     ]
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every call of this binding through another build of the library
+    (such as the race-widening debug build at RACE_WIDEN_LIB_PATH) inside the
+    block; the previous library is restored on exit."""
+    global _lib
+    prev = _lib
+    _lib = None
+    try:
+        yield load_library(path)
+    finally:
+        _lib = prev
 
 
 def header_functions(path: str = HEADER_PATH):
