@@ -79,12 +79,8 @@ namespace ssd {
 // The arithmetic is unchanged: outputs must stay bitwise equal to the
 // ordinary build's.
 __device__ __forceinline__ void race_widen_delay(int unit, int cloc, int wave) {
-    if constexpr (SSD_RACE_WIDEN != 0) {
-        const int n = (unit * 7 + cloc * 13 + wave * 5) & 15;
-        for (int k = 0; k < n; ++k) __builtin_amdgcn_s_sleep(8);
-    } else {
-        (void)unit, (void)cloc, (void)wave;
-    }
+    const int n = (unit * 7 + cloc * 13 + wave * 5) & 15;
+    for (int k = 0; k < n; ++k) __builtin_amdgcn_s_sleep(8);
 }
 
 struct FwdParams {
@@ -925,7 +921,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 load_c(hasB ? Ib : S::QT, cfb);
             }
             const float alpha = exp2f_fast(s2_last);
-            race_widen_delay(unit, cloc, wave);
+            if constexpr (SSD_RACE_WIDEN != 0) race_widen_delay(unit, cloc, wave);
             {
                 const __amdgpu_buffer_rsrc_t rout = buf_rsrc(hout, P * N * 4);
     #pragma unroll
