@@ -914,8 +914,9 @@ ssd_status_t ssd_causal_conv1d_fwd(const ssd_dims_t *dims, ssd_dtype_t io, int32
     p.HP = (int)HP;
     p.GN = (int)GN;
     p.silu = silu != 0;
-    // 64 tokens per thread, more when the grid would exceed its y limit
-    long long run = 64;
+    // 32 tokens per thread (two batches of 16), more when the grid would
+    // exceed its y limit
+    long long run = 32;
     while ((tokens + run * 4 - 1) / (run * 4) > 65535) run *= 2;
     p.run = (int)run;
     const dim3 grid((unsigned)((Cc / 8 + 63) / 64), (unsigned)((tokens + run * 4 - 1) / (run * 4)));

@@ -52,6 +52,16 @@ __device__ __forceinline__ void store8(IO *p, const float (&v)[8]) {
     *reinterpret_cast<typename Chan8<IO>::T *>(p) = t;
 }
 
+// The same as a streaming (non-temporal) store: data written once and not
+// read again by this kernel.
+template <typename IO>
+__device__ __forceinline__ void store8_stream(IO *p, const float (&v)[8]) {
+    typename Chan8<IO>::T t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = from_f32<IO>(v[e]);
+    __builtin_nontemporal_store(t, reinterpret_cast<typename Chan8<IO>::T *>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Causal depthwise convolution.
 struct ConvParams {
@@ -72,7 +82,10 @@ struct ConvParams {
 
 // Thread (chunk, run): channels 8*chunk .. 8*chunk+7 of tokens
 // [run*T, run*T + T).  A wave covers 64 consecutive chunks, so every token
-// row is read and written as contiguous 1 KB (bf16) pieces.  The run is cut
+// row is read and written as contiguous 1 KB (bf16) pieces.  Rows stream in
+// batches of 16 tokens (all 16 loads in flight before the first is used),
+// with non-temporal loads and stores: the input is read once (the W-1 rows
+// before a run are ordinary loads) and the outputs are not read here.  The run is cut
 // at sequence boundaries; at a sequence's start the width-1 previous inputs
 // come from the sequence's initial state (or are zero), and the thread that
 // holds a sequence's last token writes its final state.
@@ -156,8 +169,8 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(ConvParams p) {
                 load8(st_in + ((long long)s * (W - 1) + r) * p.Cc + c0, win[j]);
             }
         }
-        // tokens in batches of 8: all 8 rows are loaded before any is used
-        constexpr int TB = 8;
+        // tokens in batches of TB: all TB rows are loaded before any is used
+        constexpr int TB = 16;
         auto step = [&](const float (&cur)[8], long long tt) {
             float o[8];
 #pragma unroll
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(ConvParams p) {
                 acc += wt[W - 1][q] * cur[q];
                 o[q] = p.silu ? silu_f(acc) : acc;
             }
-            store8(dst + tt * dst_stride + dst_col, o);
+            store8_stream(dst + tt * dst_stride + dst_col, o);
 #pragma unroll
             for (int k = 0; k + 1 < W - 1; ++k)
 #pragma unroll
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(ConvParams p) {
             typename Chan8<IO>::T raw[TB];
 #pragma unroll
             for (int j = 0; j < TB; ++j)
-                raw[j] = *reinterpret_cast<const typename Chan8<IO>::T *>(in + (t + j) * p.Cc + c0);
+                raw[j] = __builtin_nontemporal_load(reinterpret_cast<const typename Chan8<IO>::T *>(in + (t + j) * p.Cc + c0));
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 float cur[8];
