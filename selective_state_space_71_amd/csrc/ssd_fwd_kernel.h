@@ -481,29 +481,38 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + g * N;
         const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + g * N;
 
-        // ---- first head's x and dt, then the B chunk (row layout) into LDS ----
+        // ---- every global load of the item's set-up, issued together ----
+        // The first head's x and dt, the chunk's B rows, its C rows (for the
+        // read-out, when they go to LDS) and the C rows of this wave's tiles,
+        // as branch-free buffer loads (rows past the chunk lie past the
+        // buffers' end and read 0): one memory round trip, and each group is
+        // waited for only where it is used.
         Prefetch<IO, P, N, Q> pf;
         pf.load(prm, tok0, q, h_begin, tid, wave, true);
-        {
-            constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
-            constexpr int VN = N * S::E / 16;        // vectors that hold data
-            constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
-            i32x4 bv[NV];
+        constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
+        constexpr int VN = N * S::E / 16;        // vectors that hold data
+        constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
+        const int rows_bytes = q > 0 ? ((q - 1) * bs + N) * S::E : 0;
+        const __amdgpu_buffer_rsrc_t rB = buf_rsrc(Bg, rows_bytes);
+        const __amdgpu_buffer_rsrc_t rC = buf_rsrc(Cg, rows_bytes);
+        auto row_vec = [&](int k, int &j, int &c) {   // vector k of this thread: row j, 16-byte column c
+            const int u = tid + k * S::kThreads;
+            j = u / VPR;
+            c = u - j * VPR;
+            return (Q * VPR % S::kThreads == 0 || u < Q * VPR);
+        };
+        auto row_vec_off = [&](int k) {
+            int j, c;
+            const bool ok = row_vec(k, j, c) && c < VN;
+            return ok ? (j * bs + c * (16 / S::E)) * S::E : kPastEnd;
+        };
+        i32x4 bv[NV];
     #pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int u = tid + k * S::kThreads;
-                const int j = u / VPR;
-                const int c = u - j * VPR;
-                bv[k] = i32x4{0, 0, 0, 0};
-                if (u < Q * VPR && j < q && c < VN) bv[k] = *reinterpret_cast<const i32x4 *>(Bg + j * bs + c * (16 / S::E));
-            }
+        for (int k = 0; k < NV; ++k) bv[k] = __builtin_amdgcn_raw_buffer_load_b128(rB, row_vec_off(k), 0, 0);
+        i32x4 cv[S::kCInLds ? NV : 1];
+        if constexpr (S::kCInLds) {
     #pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int u = tid + k * S::kThreads;
-                const int j = u / VPR;
-                const int c = u - j * VPR;
-                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sB + lds_off<IO, S::NP>(j, c * (16 / S::E))) = bv[k];
-            }
+            for (int k = 0; k < NV; ++k) cv[k] = __builtin_amdgcn_raw_buffer_load_b128(rC, row_vec_off(k), 0, 0);
         }
 
         // ---- this wave's row tiles, their C rows and their C B^T tiles ----
@@ -518,13 +527,18 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
     #pragma unroll
             for (int ks = 0; ks < S::NK; ++ks) {
                 const int n0 = ks * 32 + 8 * lg;
-                cf[ks] = zero_frag<Frag>();
-                if (16 * I + li < q && n0 < N) cf[ks] = *reinterpret_cast<const Frag *>(Cg + (16 * I + li) * bs + n0);
+                cf[ks] = buf_load_frag<IO>(rC, n0 < N ? ((16 * I + li) * bs + n0) * S::E : kPastEnd);
             }
         };
         Frag cga[S::NK], cgb[S::NK];
         load_c(hasA ? Ia : S::QT, cga);
         load_c(hasB ? Ib : S::QT, cgb);
+        // the B rows into LDS
+    #pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            int j, c;
+            if (row_vec(k, j, c)) *reinterpret_cast<i32x4 *>(sB + lds_off<IO, S::NP>(j, c * (16 / S::E))) = bv[k];
+        }
         if (wave == 0) pf.stage_dt(sStage, lane, q, prm.dtp);
         __syncthreads();  // B chunk and the first head's dt in LDS
         // Kept in the io precision (the MFMAs take them in it); fp32 accumulation.
@@ -569,17 +583,12 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         IO *sC = sB;
         if constexpr (S::kBtRegs) {
             __syncthreads();   // every wave is done with the B chunk
-            constexpr int VPR = S::NP * S::E / 16;
-            constexpr int VN = N * S::E / 16;
-            constexpr int NV = (Q * VPR + S::kThreads - 1) / S::kThreads;
+            if constexpr (S::kCInLds) {
     #pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int u = tid + k * S::kThreads;
-                const int j = u / VPR;
-                const int c = u - j * VPR;
-                i32x4 v = i32x4{0, 0, 0, 0};
-                if (u < Q * VPR && j < q && c < VN) v = *reinterpret_cast<const i32x4 *>(Cg + j * bs + c * (16 / S::E));
-                if (u < Q * VPR) *reinterpret_cast<i32x4 *>(sC + lds_off<IO, S::NP>(j, c * (16 / S::E))) = v;
+                for (int k = 0; k < NV; ++k) {
+                    int j, c;
+                    if (row_vec(k, j, c)) *reinterpret_cast<i32x4 *>(sC + lds_off<IO, S::NP>(j, c * (16 / S::E))) = cv[k];
+                }
             }
             // (read only after the first head's staging barrier)
         } else if constexpr (S::kAliasB) {
