@@ -715,9 +715,10 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     const long long want = 8LL * cus;
     long long hs = (w.max_entries * kh.H + want - 1) / want;
     hs = hs < 1 ? 1 : (hs > hpg ? hpg : hs);
-    // but at least two heads where the group has them: an item's set-up (its
-    // B chunk into LDS, the C B^T tiles) costs about as much as one head
-    if (hs < 2 && hpg >= 2) hs = 2;
+    // but at least three heads where the group has them: an item's set-up
+    // (its B and C rows, the C B^T tiles) costs more than one head (at the
+    // 130M-layer shape 3-head items ran 97 us, 2-head 101, 6-head 122)
+    if (hs < 3) hs = hpg < 3 ? hpg : 3;
     const int slices = (int)((hpg + hs - 1) / hs);
     pp.G = d.ngroups;
     pp.slices = slices;

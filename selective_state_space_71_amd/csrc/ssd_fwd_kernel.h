@@ -541,27 +541,49 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         }
         if (wave == 0) pf.stage_dt(sStage, lane, q, prm.dtp);
         __syncthreads();  // B chunk and the first head's dt in LDS
-        // Kept in the io precision (the MFMAs take them in it); fp32 accumulation.
-        Half gtile[S::GT];
-    #pragma unroll
-        for (int J = 0; J < S::GT; ++J) {
-            // (Ia, J) for J <= Ia, else (Ib, GT-1-J) for GT-1-J <= Ib
-    #pragma unroll
-            for (int r = 0; r < 4; ++r) gtile[J][r] = from_f32<IO>(0.f);
-            const bool useA = J <= Ia;
-            const int jt = useA ? J : S::GT - 1 - J;
-            const bool live = useA ? hasA : (hasB && jt <= Ib);
-            if (live) {
-                f32x4 acc = zero4();
-    #pragma unroll
-                for (int ks = 0; ks < S::NK; ++ks) {
-                    const Frag bfr = *reinterpret_cast<const Frag *>(sB + lds_off<IO, S::NP>(16 * jt + li, ks * 32 + 8 * lg));
-                    acc = Io<IO>::mfma(acc, bfr, useA ? cga[ks] : cgb[ks]);
-                }
-    #pragma unroll
-                for (int r = 0; r < 4; ++r) gtile[J][r] = from_f32<IO>(acc[r]);
+        // Runs f with this wave's index as a compile-time constant, so that the
+        // phases below are unrolled without any branch on the wave's row tiles.
+        auto with_wave = [&](auto f) {
+            static_assert(S::kWaves == 8, "one case per wave");
+            switch (wave) {
+            case 0: f(std::integral_constant<int, 0>{}); break;
+            case 1: f(std::integral_constant<int, 1>{}); break;
+            case 2: f(std::integral_constant<int, 2>{}); break;
+            case 3: f(std::integral_constant<int, 3>{}); break;
+            case 4: f(std::integral_constant<int, 4>{}); break;
+            case 5: f(std::integral_constant<int, 5>{}); break;
+            case 6: f(std::integral_constant<int, 6>{}); break;
+            default: f(std::integral_constant<int, 7>{}); break;
             }
-        }
+        };
+        // Kept in the io precision (the MFMAs take them in it); fp32 accumulation.
+        // Tile (Ia, J) for J <= Ia, else (Ib, GT-1-J); rows past the chunk hold
+        // zeros in B and C, so their tiles come out 0 without a test.  The K
+        // loop is outermost, so the tiles' independent MFMA chains interleave.
+        Half gtile[S::GT];
+        with_wave([&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            f32x4 acc[S::GT];
+    #pragma unroll
+            for (int J = 0; J < S::GT; ++J) acc[J] = zero4();
+    #pragma unroll
+            for (int ks = 0; ks < S::NK; ++ks) {
+    #pragma unroll
+                for (int J = 0; J < S::GT; ++J) {
+                    const bool useA = J <= W;
+                    const bool live = useA ? W < S::QT : S::kTwoTiles;
+                    const int jt = useA ? J : S::GT - 1 - J;
+                    if (live) {
+                        const Frag bfr = *reinterpret_cast<const Frag *>(sB + lds_off<IO, S::NP>(16 * jt + li, ks * 32 + 8 * lg));
+                        acc[J] = Io<IO>::mfma(acc[J], bfr, useA ? cga[ks] : cgb[ks]);
+                    }
+                }
+            }
+    #pragma unroll
+            for (int J = 0; J < S::GT; ++J)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) gtile[J][r] = from_f32<IO>(acc[J][r]);
+        });
 
         const int wn = wave % S::WN;
         const int wp = wave / S::WN;
@@ -646,21 +668,6 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 }
             }
             return m;
-        };
-        // Runs f with this wave's index as a compile-time constant, so that the
-        // phases below are unrolled without any branch on the wave's row tiles.
-        auto with_wave = [&](auto f) {
-            static_assert(S::kWaves == 8, "one case per wave");
-            switch (wave) {
-            case 0: f(std::integral_constant<int, 0>{}); break;
-            case 1: f(std::integral_constant<int, 1>{}); break;
-            case 2: f(std::integral_constant<int, 2>{}); break;
-            case 3: f(std::integral_constant<int, 3>{}); break;
-            case 4: f(std::integral_constant<int, 4>{}); break;
-            case 5: f(std::integral_constant<int, 5>{}); break;
-            case 6: f(std::integral_constant<int, 6>{}); break;
-            default: f(std::integral_constant<int, 7>{}); break;
-            }
         };
         // Row tiles of wave W: tile a = W, tile b = 2 kWaves - 1 - W (chunks of
         // 2 kWaves tiles); each tile's decay block R, and its explicit K steps
