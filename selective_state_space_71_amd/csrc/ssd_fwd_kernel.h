@@ -238,14 +238,20 @@ constexpr int kPastEnd = 0x40000000;   // a byte offset beyond every buffer of t
 // and lgkmcnt (15) at their no-wait maxima.
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <typename IO>
+// Cache-policy operand of a buffer access that streams data used once (the x
+// rows of a head, the y rows): non-temporal, so that these lines are the
+// first the XCD's L2 gives up and the boundary states handed from chunk to
+// chunk stay there.
+constexpr int kStream = 2;   // nt
+
+template <typename IO, int AUX = 0>
 __device__ __forceinline__ typename Io<IO>::Frag buf_load_frag(__amdgpu_buffer_rsrc_t r, int off) {
     typedef typename Io<IO>::Frag Frag;
     if constexpr (sizeof(IO) == 2) {
-        return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
     } else {
-        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, AUX);
         return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 }
@@ -327,7 +333,7 @@ struct Prefetch {
     // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  With 64
     // channels (eight blocks), the eight lanes of a run take the eight blocks
     // of one token group, so a wave's load instruction reads whole 128-byte
-    // rows of x; lane bit 3 and lane bits 4-5 pick the token group, which with
+    // rows of x (non-temporal: each row is read once); lane bit 3 and lane bits 4-5 pick the token group, which with
     // x_lds_off's swizzle keeps the 8-byte staging writes of 32 lanes on
     // distinct banks.  Other widths: sixteen consecutive units take sixteen
     // consecutive token groups of one channel block.
@@ -357,7 +363,7 @@ struct Prefetch {
             for (int t = 0; t < 4; ++t) {
                 const int i = 4 * t4 + t;   // i >= q lies past the buffer's end
                 const bool uok = NUNIT % S::kThreads == 0 || u < NUNIT;
-                x[k][t] = buf_load_frag<IO>(rx, uok ? (i * xs + p0) * S::E : kPastEnd);
+                x[k][t] = buf_load_frag<IO, PB == 8 ? kStream : 0>(rx, uok ? (i * xs + p0) * S::E : kPastEnd);
             }
         }
         const int hm = h / prm.hsub, Hm = prm.H / prm.hsub;
@@ -1028,7 +1034,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                     // The wave's rows go through LDS (xh^T's space, dead since
                     // the compute phase) and leave as whole 128-byte rows, one
                     // 16-byte store per lane, rather than as 32-byte pieces of
-                    // four stores.  Only this wave touches these rows.
+                    // four stores, non-temporal (y is not read again).  Only
+                    // this wave touches these rows.
                     IO *sY = sXh;
                     auto y_to_lds = [&](int I, const f32x4 (&o)[S::PT], const f32x4 (&accY)[S::PT]) {
                         const int i_row = 16 * I + li;
@@ -1047,7 +1054,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                             const int row = 16 * I + 8 * k + (lane >> 3);
                             const int col = 8 * (lane & 7);
                             const i32x4 v = *reinterpret_cast<const i32x4 *>(sY + y_lds_off(row, col));
-                            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (row * xs + col) * S::E, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (row * xs + col) * S::E, 0, kStream);
                         }
                     };
                     if (T.HA) y_to_lds(T.IA, oa, accYa);
