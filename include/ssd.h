@@ -357,7 +357,10 @@ ssd_status_t ssd_gated_rmsnorm_fwd(int64_t rows, int32_t dim, int32_t group_size
  *               2 * tokens/64 * nheads * headdim * dstate * 4 bytes).
  *
  * Deterministic (fixed reduction orders, no atomics).  Supported: headdim in
- * {16, 32, 64}, dstate in {16, 32, 64, 128} (bf16) or {16, 32, 64} (fp32).
+ * {16, 32, 64, 128}, dstate in {16, 32, 64, 128} (bf16) or {16, 32, 64}
+ * (fp32); head dim 128 runs as two kernel heads of 64 channels (every state
+ * row depends only on its own channel of x), whose ddt, dA and dD terms are
+ * added in a fixed order.  Other sizes return SSD_ERR_UNSUPPORTED.
  * Outputs must not overlap each other, the inputs or the workspace.
  */
 size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims_t *dims, ssd_dtype_t io_dtype);

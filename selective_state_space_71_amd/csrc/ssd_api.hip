@@ -304,8 +304,9 @@ static bool conv_launch(int width, const ConvParams &p, dim3 grid, hipStream_t s
     }
 }
 
-// Backward: headdim 16..64 with dstate 16..128 (bf16) or 16..64 (fp32), where
-// the chunk kernel's tiles fit in LDS.
+// Backward: kernel head dims 16..64 with dstate 16..128 (bf16) or 16..64
+// (fp32), where the chunk kernel's tiles fit in LDS (head dim 128 runs as two
+// kernel heads of 64).
 template <typename IO, int P, int N>
 static bool bwd_try(int pp, int nn, const BwdParams &p, unsigned units, unsigned n_chunks_max, bool launch,
                     hipStream_t st) {
@@ -987,9 +988,10 @@ bool bwd_ws(const ssd_dims_t &d, bool varlen, BwdWs *w) {
     w->seqstart = align_up((size_t)w->max_chunks * 16, 256);
     w->states = align_up(w->seqstart + (size_t)(d.nseq + 1) * 4, 256);
     w->radj = align_up(w->states + (size_t)(w->max_chunks + d.nseq) * st, 256);
+    const long long kh = kernel_heads(d).H;   // per-chunk dA, dD partials per kernel head
     w->partA = align_up(w->radj + (size_t)w->max_chunks * st, 256);
-    w->partD = align_up(w->partA + (size_t)w->max_chunks * d.nheads * 4, 256);
-    w->total = align_up(w->partD + (size_t)w->max_chunks * d.nheads * 4, 256);
+    w->partD = align_up(w->partA + (size_t)w->max_chunks * kh * 4, 256);
+    w->total = align_up(w->partD + (size_t)w->max_chunks * kh * 4, 256);
     return true;
 }
 
@@ -1000,10 +1002,11 @@ ssd_status_t bwd_shape_check(const ssd_dims_t *dims, ssd_dtype_t io, bool varlen
     if (!dims_ok(d)) return SSD_ERR_SHAPE;
     if (varlen ? (d.batch != 1 || d.nseq > 65536) : d.nseq != d.batch) return SSD_ERR_SHAPE;
     ssd::BwdParams dummy{};
-    const bool built = (io == SSD_BF16) ? ssd::bwd_dispatch<ssd::bf16>(d.headdim, d.dstate, dummy, 0, 0, false, nullptr)
-                                        : ssd::bwd_dispatch<float>(d.headdim, d.dstate, dummy, 0, 0, false, nullptr);
+    const KHeads kh = kernel_heads(d);
+    const bool built = (io == SSD_BF16) ? ssd::bwd_dispatch<ssd::bf16>(kh.P, d.dstate, dummy, 0, 0, false, nullptr)
+                                        : ssd::bwd_dispatch<float>(kh.P, d.dstate, dummy, 0, 0, false, nullptr);
     if (!built) return SSD_ERR_UNSUPPORTED;
-    if ((long long)d.batch * d.seqlen > INT_MAX / 2 || (long long)d.nseq * d.nheads > INT_MAX) return SSD_ERR_SHAPE;
+    if ((long long)d.batch * d.seqlen > INT_MAX / 2 || (long long)d.nseq * kh.H > INT_MAX) return SSD_ERR_SHAPE;
     return SSD_OK;
 }
 }  // namespace
@@ -1093,13 +1096,15 @@ ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const vo
     p.radj = reinterpret_cast<float *>(ws + w.radj);
     p.partA = reinterpret_cast<float *>(ws + w.partA);
     p.partD = reinterpret_cast<float *>(ws + w.partD);
-    p.H = d.nheads;
+    const KHeads kh = kernel_heads(d);
+    p.H = kh.H;
+    p.hsub = kh.hsub;
     p.G = d.ngroups;
     p.nseq = d.nseq;
-    const unsigned units = (unsigned)d.nseq * (unsigned)d.nheads;
+    const unsigned units = (unsigned)d.nseq * (unsigned)kh.H;
     const bool ok = (io == SSD_BF16)
-                        ? ssd::bwd_dispatch<ssd::bf16>(d.headdim, d.dstate, p, units, (unsigned)w.max_chunks, true, s)
-                        : ssd::bwd_dispatch<float>(d.headdim, d.dstate, p, units, (unsigned)w.max_chunks, true, s);
+                        ? ssd::bwd_dispatch<ssd::bf16>(kh.P, d.dstate, p, units, (unsigned)w.max_chunks, true, s)
+                        : ssd::bwd_dispatch<float>(kh.P, d.dstate, p, units, (unsigned)w.max_chunks, true, s);
     if (!ok) return SSD_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(ssd::ssd_bwd_reduce_kernel, dim3(d.nheads), dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;

@@ -55,7 +55,15 @@ struct BwdParams {
     float *states;                // [n_chunks + nseq][H][P][N]: H_0 .. H_T of every sequence
     float *radj;                  // [n_chunks][H][P][N]: R_c
     float *partA, *partD;         // [n_chunks][H]
+    // H counts kernel heads of P channels.  A head dim wider than the
+    // kernel's (128 on 64-channel kernels) runs as `hsub` consecutive kernel
+    // heads per model head: x, dy, dx and the states then have the layout of
+    // H = hsub * nheads heads (each state row depends only on its own channel
+    // of x and on the head's shared dt, A, B, C), while dt, A, D, ddt, dA and
+    // dD are indexed by the model head h / hsub, and the sub-heads' terms of
+    // ddt, dA and dD are added in a fixed order.
     int H, G, nseq;
+    int hsub;                     // kernel heads per model head (1 or 2)
 };
 
 // Operand accessors return A[m][k] (row m of the A operand) or B[k][n]; one
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_kernel(BwdParams p) {
     const long long PN = (long long)P * N;
     const IO *ug = reinterpret_cast<const IO *>(MODE == 0 ? p.x : p.dy);
     const IO *vg = reinterpret_cast<const IO *>(MODE == 0 ? p.B : p.C);
-    const float Ah = p.A[h];
+    const float Ah = p.A[h / p.hsub];
 
     // Wave w holds state tiles t = w + 4 k, (pt, nt) = (t % PT, t / PT):
     // element r of tile k is state[pt*16 + li][nt*16 + 4 lg + r].
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_scan_kernel(BwdParams p) {
         stage_rows<IO, P>(su, ug, t0, q, (long long)p.H * P, (long long)h * P, tid);
         stage_rows<IO, N>(sv, vg, t0, q, (long long)p.G * N, (long long)g * N, tid);
         if (wave == 0) {
-            const float d = lane < q ? p.dt[(t0 + lane) * p.H + h] : 0.f;
+            const float d = lane < q ? p.dt[(t0 + lane) * (p.H / p.hsub) + h / p.hsub] : 0.f;
             const float sc = wave_inclusive_sum(d * Ah) * kLog2e;   // s * log2(e)
             const float slast = __shfl(sc, 63, 64);
             swt[lane] = MODE == 0 ? __builtin_amdgcn_exp2f(slast - sc) * d : __builtin_amdgcn_exp2f(sc);
@@ -291,6 +299,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
     for (int nt = 0; nt < NT; ++nt) dBacc[nt] = dCacc[nt] = zero4();
     const int row0 = wave * 16;
 
+    float ddt_sub = 0.f;   // ddt of a model head summed over its kernel heads (wave 0)
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         __syncthreads();   // the previous head's tiles are no longer read
@@ -305,9 +314,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
             Rs[i] = rv;
             hrd += hv * rv;
         }
-        const float Ah = p.A[h];
+        const float Ah = p.A[h / p.hsub];
         if (wave == 0) {
-            const float d = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
+            const float d = lane < q ? p.dt[(t0 + lane) * (H / p.hsub) + h / p.hsub] : 0.f;
             const float sc = wave_inclusive_sum(d * Ah) * kLog2e;
             const float slast = __shfl(sc, 63, 64);
             s2[lane] = sc;
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
         }
 
         // dx = M^T dY + diag(w) B R^T + D dY, row band w
-        const float Dh = p.D ? p.D[h] : 0.f;
+        const float Dh = p.D ? p.D[h / p.hsub] : 0.f;
         IO *dxg = reinterpret_cast<IO *>(p.dx);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
@@ -452,7 +461,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
             float ds = rowZ[j] - d * colZ[j] + offC[j] - d * offB[j] + (j == q - 1 ? rh : 0.f);
             const float tot = bwd_wave_sum(ds);
             const float da = tot - wave_inclusive_sum(ds) + ds;    // sum over i >= j
-            if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + colZ[j] + offB[j];
+            const float v = Ah * da + colZ[j] + offB[j];
+            ddt_sub = (h % p.hsub == 0) ? v : ddt_sub + v;   // the model head's sub-heads, in order
+            if (j < q && h % p.hsub == p.hsub - 1) p.ddt[(t0 + j) * (H / p.hsub) + h / p.hsub] = ddt_sub;
             const float pa = bwd_wave_sum(d * da);
             if (lane == 0) p.partA[(long long)ci * H + h] = pa;
         }
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             hr[k] = zero4();
             if (i < 4 * SP4) hr[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
         }
-        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * H + h] : 0.f;
+        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * (H / p.hsub) + h / p.hsub] : 0.f;
         if (with_r) load_r(h);
     };
 
@@ -610,6 +621,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
     for (int k = 0; k < NT2; ++k) dBacc[k] = dCacc[k] = zero4();
 
     if (hpg > 0) load_head(g * hpg, true);
+    float ddt_sub = 0.f;   // ddt of a model head summed over its kernel heads (wave 0)
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         // Lane indices re-derived per head: the tiles span more LDS than a ds
@@ -653,7 +665,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         }
         hrd = bwd_wave_sum(hrd);
         if (lane == 0) hrp[wave] = hrd;
-        const float Ah = p.A[h];
+        const float Ah = p.A[h / p.hsub];
         if (wave == 0) {
             const float sc = wave_inclusive_sum(dtr * Ah) * kLog2e;
             const float slast = __shfl(sc, 63, 64);
@@ -714,7 +726,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
 
         if (hh + 1 < hpg) load_r(h + 1);
         // dx = M^T dY + diag(w) B R^T + D dY (this band, this half's columns)
-        const float Dh = p.D ? p.D[h] : 0.f;
+        const float Dh = p.D ? p.D[h / p.hsub] : 0.f;
         bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
         // computed transposed (rows head-dim, columns tokens), so that each lane
         // holds 4 consecutive head-dim entries of one token: one 8-byte dy read
@@ -795,7 +807,9 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
             const float ds = rz - d * cz + oc_ - d * ob_ + (j == q - 1 ? rh : 0.f);
             const float tot = bwd_wave_sum(ds);
             const float da = tot - wave_inclusive_sum(ds) + ds;
-            if (j < q) p.ddt[(t0 + j) * H + h] = Ah * da + cz + ob_;
+            const float v = Ah * da + cz + ob_;
+            ddt_sub = (h % p.hsub == 0) ? v : ddt_sub + v;   // the model head's sub-heads, in order
+            if (j < q && h % p.hsub == p.hsub - 1) p.ddt[(t0 + j) * (H / p.hsub) + h / p.hsub] = ddt_sub;
             const float pa = bwd_wave_sum(d * da);
             if (lane == 0) p.partA[(long long)ci * H + h] = pa;
         }
@@ -880,7 +894,7 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
     const long long PN = (long long)P * N;
     const bf16 *ug = reinterpret_cast<const bf16 *>(mode == 0 ? p.x : p.dy);
     const bf16 *vg = reinterpret_cast<const bf16 *>(mode == 0 ? p.B : p.C);
-    const float Ah = p.A[h];
+    const float Ah = p.A[h / p.hsub];
 
     f32x4 st[TPW];
     const float *st0 = mode == 0 ? p.init_state : p.dfinal;
@@ -924,7 +938,7 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
             vr[k] = zero_frag<bf16x8>();
             if (j < q) vr[k] = *reinterpret_cast<const bf16x8 *>(vg + ((t0 + j) * p.G + g) * N + c8);
         }
-        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * p.H + h] : 0.f;
+        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * (p.H / p.hsub) + h / p.hsub] : 0.f;
     };
     if (nc > 0) load_chunk(mode == 0 ? 0 : nc - 1);
 
@@ -985,16 +999,19 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
     if (mode == 1 && p.dinit) store_state(p.dinit + ((long long)s * p.H + h) * PN);
 }
 
-// dA[h], dD[h]: sums of the per-chunk partials, one workgroup per head, in a
-// fixed order (strided partial sums, then a fixed tree).
+// dA[h], dD[h]: sums of the per-chunk partials of the model head's kernel
+// heads, one workgroup per model head, in a fixed order (strided partial
+// sums, then a fixed tree).
 __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdParams p) {
     __shared__ float red[2][4];
     const int h = blockIdx.x;
     const int n_chunks = p.seq_chunk_start[p.nseq];
     float a = 0.f, d = 0.f;
     for (int c = threadIdx.x; c < n_chunks; c += 256) {
-        a += p.partA[(long long)c * p.H + h];
-        d += p.partD[(long long)c * p.H + h];
+        for (int u = 0; u < p.hsub; ++u) {
+            a += p.partA[(long long)c * p.H + h * p.hsub + u];
+            d += p.partD[(long long)c * p.H + h * p.hsub + u];
+        }
     }
     a = bwd_wave_sum(a);
     d = bwd_wave_sum(d);

@@ -57,6 +57,11 @@ def _ref(inp, unit_mask=None):
     ("f32", 1, 100, 2, 16, 16, 1, None),
     ("f32", 2, 70, 2, 64, 64, 1, None),
     ("f32", 1, 90, 4, 32, 32, 2, [30, 60]),
+    # head dim 128: two kernel heads of 64 channels per model head
+    ("bf16", 2, 200, 4, 128, 128, 1, None),
+    ("bf16", 1, 200, 4, 128, 64, 2, [64, 0, 1, 100, 35]),
+    ("f32", 1, 150, 2, 128, 64, 1, None),
+    ("f32", 1, 90, 4, 128, 32, 2, [30, 60]),
 ])
 def test_backward_small(io, b, L, H, P, N, G, lengths):
     inp = _inputs(io, b, L, H, P, N, G, seed=L + H + N, lengths=lengths)
