@@ -30,15 +30,21 @@ bool fwd_dispatch_f32(int p, int n, int q, const FwdParams &prm, long long max_e
 // chunk index first and sequence second, so the predecessor of an entry
 // (same sequence, previous chunk) always has a smaller index.  A work item
 // is (entry, group, head slice); all items of one (sequence, group, slice)
-// chain go to the same XCD (round robin over chains), and each XCD's list
-// keeps the entry order, so an item's predecessor is always earlier in the
-// same list.  The kernel also clears the tickets, the error word and the
-// per-(sequence, head) progress flags, and writes the final state of empty
-// packed sequences (the initial state, or zero).
+// chain go to the same XCD, and each XCD's list keeps the entry order, so an
+// item's predecessor is always earlier in the same list.  Dense batches (all
+// sequences of one length) give each XCD a contiguous block of chains in
+// (sequence, group, slice) order, so that the slices of a sequence share few
+// XCDs and their B, C and dt rows are fetched by few L2s; packed batches go
+// round robin over chains (their sequences differ in length, and a block of
+// whole sequences would unbalance the XCDs).  The kernel also clears the
+// tickets, the error word and the per-(sequence, head) progress flags, and
+// writes the final state of empty packed sequences (the initial state, or
+// zero).
 struct PrepParams {
     const int *cu_seqlens;  // null for a dense batch
     int batch, seqlen, nseq, H, Q;
     int G, slices, n_xcd;
+    int flag_stride;        // ints between consecutive progress flags
     int max_entries;        // capacity of the chunk table
     int state_elems;        // P * N
     int4 *chunks;
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
     const int tid = threadIdx.x;
     const int Q = p.Q;
     __shared__ int cnt[16], run[16];
-    for (int u = tid; u < p.nseq * p.H; u += 256) p.flags[u] = 0;
+    for (int u = tid; u < p.nseq * p.H; u += 256) p.flags[(long long)u * p.flag_stride] = 0;
     if (tid < 16) {
         p.tickets[tid] = 0;
         cnt[tid] = 0;
@@ -152,7 +158,28 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
     __syncthreads();
     const int GS = p.G * p.slices;
     const int n_items = n_entries * GS;
-    if (GS % p.n_xcd == 0) {
+    const int n_chains = p.nseq * GS;
+    if (dense && n_chains % p.n_xcd == 0) {
+        // XCD x runs chains [x per, (x + 1) per) of the (sequence, group,
+        // slice) order; for every chunk index it holds one item per chain, in
+        // chain order, which is also the entry order (closed form)
+        const int per = n_chains / p.n_xcd;
+        const int nc = n_entries / p.nseq;
+        if (tid < 16) {
+            p.xcd_count[tid] = tid < p.n_xcd ? nc * per : 0;
+            p.xcd_offset[tid] = (tid < p.n_xcd ? tid : p.n_xcd) * nc * per;
+        }
+        for (int i = tid; i < n_items; i += 256) {
+            const int e = i / GS;
+            const int j = i - e * GS;
+            const int c = e / p.nseq;
+            const int k = (e - c * p.nseq) * GS + j;   // chain
+            const int x = k / per;
+            p.items[x * nc * per + c * per + (k - x * per)] = i;
+        }
+        return;
+    }
+    if (!dense && GS % p.n_xcd == 0) {
         // item j of every entry goes to XCD j mod n_xcd (the sequence term is
         // a multiple of n_xcd): the lists have a closed form, written in parallel
         const int per = GS / p.n_xcd;
@@ -171,7 +198,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
     auto xcd_of = [&](int i) {
         const int e = i / GS;
         const int seq = e < kSeqCache ? sseq[e] : p.chunks[e].x;
-        return (seq * GS + (i - e * GS)) % p.n_xcd;
+        const long long k = (long long)seq * GS + (i - e * GS);   // chain
+        return dense ? (int)(k * p.n_xcd / n_chains) : (int)(k % p.n_xcd);
     };
     for (int i = tid; i < n_items; i += 256) atomicAdd(&cnt[xcd_of(i)], 1);
     __syncthreads();
@@ -501,6 +529,14 @@ struct WsLayout {
 // 68 entry count, [128,192) items per XCD, [192,256) list offsets.
 constexpr size_t kWsTickets = 0, kWsError = 64, kWsEntries = 68, kWsXcdCount = 128, kWsXcdOffset = 192;
 
+// Progress flags one 128-byte line apart while they take at most 4 MiB: the
+// workgroups of an XCD poll and bump the flags of neighbouring heads at the
+// same time, and flags sharing a line serialize those accesses (130M-layer
+// shape 96 -> 87 us).  Beyond that, packed.
+int flag_stride(const ssd_dims_t &d) {
+    return (long long)d.nseq * kernel_heads(d).H <= 32768 ? 32 : 1;
+}
+
 // Workspace: header; per-(sequence, head) flags; chunk table; per-XCD item
 // lists (at most entries x heads items); packed-batch scratch; fp32
 // boundary-state buffer.
@@ -509,7 +545,7 @@ bool ws_layout(const ssd_dims_t &d, int Q, bool varlen, WsLayout *w) {
     const int kh = kernel_heads(d).H;
     w->max_entries = varlen ? nc + d.nseq : nc * d.batch;
     w->flags = 256;
-    w->chunks = align_up(w->flags + (size_t)d.nseq * kh * 4, 256);
+    w->chunks = align_up(w->flags + (size_t)d.nseq * kh * 4 * flag_stride(d), 256);
     w->items = align_up(w->chunks + (size_t)w->max_entries * 16, 256);
     w->scratch = align_up(w->items + (size_t)w->max_entries * kh * 4, 256);
     w->state = align_up(w->scratch + (size_t)(d.nseq + 1) * 4, 256);
@@ -726,6 +762,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     pp.max_entries = (int)w.max_entries;
     pp.n_xcd = num_xcds();
     if (pp.n_xcd < 1) return SSD_ERR_HIP;
+    pp.flag_stride = flag_stride(d);
     hipLaunchKernelGGL(ssd::ssd_prep_kernel, dim3(1), dim3(256), 0, s, pp);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
 
@@ -748,6 +785,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, ssd_dtype_t io, int32_t chunk_len,
     fp.xcd_offset = pp.xcd_offset;
     fp.n_xcd = pp.n_xcd;
     fp.flags = pp.flags;
+    fp.flag_stride = pp.flag_stride;
     fp.error = pp.error;
     fp.H = kh.H;
     fp.hsub = kh.hsub;

@@ -102,6 +102,7 @@ struct FwdParams {
     const int *xcd_offset;    // start of each XCD's list
     int n_xcd;
     int *flags;               // per (sequence, head): published state parts (kWaves per chunk)
+    int flag_stride;          // ints between consecutive flags (one cache line apart, or packed)
     int *error;
     // H counts kernel heads of P channels.  A head dim wider than the kernel
     // tile (P = 128 on 64-wide tiles) runs as `hsub` consecutive kernel heads
@@ -732,7 +733,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 // (compared only after the scan, so that the scan does not wait for it)
                 // (wave 0 reads it; an empty buffer elsewhere and for the first chunk)
                 int flagv = __builtin_bit_cast(
-                    int, buf_load_f32<kStateLoad>(buf_rsrc(prm.flags + unit, wave == 0 && cloc > 0 ? 4 : 0), 0));
+                    int, buf_load_f32<kStateLoad>(buf_rsrc(prm.flags + (long long)unit * prm.flag_stride, wave == 0 && cloc > 0 ? 4 : 0), 0));
                 // Every wave scans the whole chunk (R tokens per lane, from the
                 // staged dt) and writes the per-token vectors of its own Q/8
                 // tokens (lanes 8 wave .. 8 wave + 7).
@@ -924,7 +925,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             if (!early || S::kAliasH) {
                 if (!early && tid == 0) {
                     int it = 0;
-                    while (__hip_atomic_load(prm.flags + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                    while (__hip_atomic_load(prm.flags + (long long)unit * prm.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                            S::kWaves * cloc) {
                         __builtin_amdgcn_s_sleep(1);
                         if (++it > (1 << 22)) {
@@ -1027,7 +1028,7 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                 // prefetch's loads, the last ones issued, has completed
                 __builtin_amdgcn_s_waitcnt(vmcnt_only(Prefetch<IO, P, N, Q>::kLoads));
                 // (lane 0 adds; the other lanes' offsets lie past the counter)
-                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, buf_rsrc(prm.flags + unit, 4), lane == 0 ? 0 : kPastEnd,
+                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, buf_rsrc(prm.flags + (long long)unit * prm.flag_stride, 4), lane == 0 ? 0 : kPastEnd,
                                                                      0, 0);
                 const __amdgpu_buffer_rsrc_t ry = buf_rsrc(yg, q * xs * S::E);   // rows i >= q lie past its end
                 if constexpr (S::kYViaLds) {
