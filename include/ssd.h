@@ -354,13 +354,20 @@ ssd_status_t ssd_gated_rmsnorm_fwd(int64_t rows, int32_t dim, int32_t group_size
  *   workspace   >= ssd_chunk_scan_bwd_workspace_size(dims, io_dtype) bytes,
  *               256-byte aligned, not used by another call in flight (holds
  *               every chunk-boundary state and state gradient: about
- *               2 * tokens/64 * nheads * headdim * dstate * 4 bytes).
+ *               2 * tokens/64 * nheads * headdim * dstate * 4 bytes; for a
+ *               state dim run in slices, see below, that of one slice plus
+ *               the slices' inputs and dx, ddt terms).
  *
  * Deterministic (fixed reduction orders, no atomics).  Supported: headdim in
- * {16, 32, 64, 128}, dstate in {16, 32, 64, 128} (bf16) or {16, 32, 64}
- * (fp32); head dim 128 runs as two kernel heads of 64 channels (every state
- * row depends only on its own channel of x), whose ddt, dA and dD terms are
- * added in a fixed order.  Other sizes return SSD_ERR_UNSUPPORTED.
+ * {16, 32, 64, 128}, dstate in {16, 32, 64, 128, 256}, both io dtypes; other
+ * sizes return SSD_ERR_UNSUPPORTED.  Head dim 128 runs as two kernel heads of
+ * 64 channels (every state row depends only on its own channel of x), whose
+ * ddt, dA and dD terms are added in a fixed order.  State dims beyond the
+ * kernels' (bf16: 256; fp32: 128 and 256) run once per slice of 128 (bf16) or
+ * 64 (fp32) state columns: every state column evolves on its own and y is a
+ * sum over them, so each slice gives its columns of dB, dC and dinit and one
+ * term of dx, ddt and dA, added slice by slice (dx rounded to the io dtype
+ * once); the slices' B, C and states are copied through the workspace.
  * Outputs must not overlap each other, the inputs or the workspace.
  */
 size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims_t *dims, ssd_dtype_t io_dtype);

@@ -1033,75 +1033,86 @@ bool bwd_ws(const ssd_dims_t &d, bool varlen, BwdWs *w) {
     return true;
 }
 
+// State dim of the backward kernels: dstate itself where built, else the
+// largest built state dim that divides it (0: none).  Above it the backward
+// runs once per slice of the state dim: every state column n evolves on its
+// own (h[p, n] depends only on B[:, n]), and y, hence every gradient, is a sum
+// over n, so each slice's run gives that slice's columns of dB, dC and dinit
+// and one term of dx, ddt and dA (dD does not depend on n).
+int bwd_kernel_n(const ssd_dims_t &d, ssd_dtype_t io) {
+    const KHeads kh = kernel_heads(d);
+    ssd::BwdParams dummy{};
+    auto built = [&](int n) {
+        return (io == SSD_BF16) ? ssd::bwd_dispatch<ssd::bf16>(kh.P, n, dummy, 0, 0, false, nullptr)
+                                : ssd::bwd_dispatch<float>(kh.P, n, dummy, 0, 0, false, nullptr);
+    };
+    if (built(d.dstate)) return d.dstate;
+    if (d.dstate != 128 && d.dstate != 256) return 0;   // the forward's other state dims
+    for (int n = 128; n >= 16; n /= 2)
+        if (n < d.dstate && d.dstate % n == 0 && built(n)) return n;
+    return 0;
+}
+
 ssd_status_t bwd_shape_check(const ssd_dims_t *dims, ssd_dtype_t io, bool varlen) {
     if (!dims) return SSD_ERR_NULL_PTR;
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_DTYPE;
     const ssd_dims_t &d = *dims;
     if (!dims_ok(d)) return SSD_ERR_SHAPE;
     if (varlen ? (d.batch != 1 || d.nseq > 65536) : d.nseq != d.batch) return SSD_ERR_SHAPE;
-    ssd::BwdParams dummy{};
-    const KHeads kh = kernel_heads(d);
-    const bool built = (io == SSD_BF16) ? ssd::bwd_dispatch<ssd::bf16>(kh.P, d.dstate, dummy, 0, 0, false, nullptr)
-                                        : ssd::bwd_dispatch<float>(kh.P, d.dstate, dummy, 0, 0, false, nullptr);
-    if (!built) return SSD_ERR_UNSUPPORTED;
-    if ((long long)d.batch * d.seqlen > INT_MAX / 2 || (long long)d.nseq * kh.H > INT_MAX) return SSD_ERR_SHAPE;
+    if (bwd_kernel_n(d, io) == 0) return SSD_ERR_UNSUPPORTED;
+    if ((long long)d.batch * d.seqlen > INT_MAX / 2 || (long long)d.nseq * kernel_heads(d).H > INT_MAX)
+        return SSD_ERR_SHAPE;
     return SSD_OK;
 }
-}  // namespace
 
-size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims_t *dims, ssd_dtype_t io) {
-    if (!dims) return 0;
-    if (bwd_shape_check(dims, io, true) != SSD_OK && bwd_shape_check(dims, io, false) != SSD_OK) return 0;
-    BwdWs a{}, b{};
-    bwd_ws(*dims, true, &a);
-    bwd_ws(*dims, false, &b);
-    return a.total > b.total ? a.total : b.total;
-}
+// Workspace of a state-dim-split backward: the kernels' own workspace for one
+// slice, then the slice's inputs (B, C, initial state, final-state gradient),
+// its dB, dC and dinit, and every slice's dx, ddt, dA and dD terms.
+struct BwdSplitWs {
+    size_t B, C, init, dfin, dinit, dB, dC, dx, ddt, dA, dD, total;
+    int kn, nsplit;
+    BwdWs inner;
+};
 
-ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const void *x, const float *dt,
-                                const float *A, const void *B, const void *C, const float *D,
-                                const float *init_state, const int32_t *cu_seqlens, const void *dy,
-                                const float *dfinal_state, void *dx, float *ddt, float *dA, float *dB, float *dC,
-                                float *dD, float *dinit_state, void *workspace, size_t workspace_bytes,
-                                void *stream) {
-    const bool varlen = cu_seqlens != nullptr;
-    ssd_status_t st = bwd_shape_check(dims, io, varlen);
-    if (st != SSD_OK) return st;
-    const ssd_dims_t &d = *dims;
-    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !dD) return SSD_ERR_NULL_PTR;
-    if (!workspace) return SSD_ERR_WORKSPACE;
-    const void *al16[] = {x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA, dB, dC, dD, dinit_state};
-    for (const void *q : al16)
-        if (q && !aligned(q, 16)) return SSD_ERR_ALIGNMENT;
-    if (!aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
-    if (cu_seqlens && !aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
-    BwdWs w{};
-    bwd_ws(d, varlen, &w);
-    if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
-
+bool bwd_split_ws(const ssd_dims_t &d, ssd_dtype_t io, bool varlen, BwdSplitWs *w) {
+    w->kn = bwd_kernel_n(d, io);
+    w->nsplit = w->kn ? d.dstate / w->kn : 0;
+    ssd_dims_t dk = d;
+    dk.dstate = w->kn;
+    bwd_ws(dk, varlen, &w->inner);
     const size_t E = (io == SSD_BF16) ? 2 : 4;
     const size_t tokens = (size_t)d.batch * d.seqlen;
-    const size_t nx = tokens * d.nheads * d.headdim, nbc = tokens * d.ngroups * d.dstate;
-    const size_t nst = (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4;
-    const Range ins[] = {rng(x, nx * E), rng(dt, tokens * d.nheads * 4), rng(A, (size_t)d.nheads * 4),
-                         rng(B, nbc * E), rng(C, nbc * E), rng(D, D ? (size_t)d.nheads * 4 : 0),
-                         rng(init_state, init_state ? nst : 0), rng(dy, nx * E),
-                         rng(dfinal_state, dfinal_state ? nst : 0),
-                         rng(cu_seqlens, varlen ? (size_t)(d.nseq + 1) * 4 : 0), rng(workspace, w.total)};
-    const Range outs[] = {rng(dx, nx * E), rng(ddt, tokens * d.nheads * 4), rng(dA, (size_t)d.nheads * 4),
-                          rng(dB, nbc * 4), rng(dC, nbc * 4), rng(dD, (size_t)d.nheads * 4),
-                          rng(dinit_state, dinit_state ? nst : 0)};
-    for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
-        for (const Range &r : ins)
-            if (overlap(outs[a], r)) return SSD_ERR_ALIAS;
-        for (size_t b = a + 1; b < sizeof(outs) / sizeof(outs[0]); ++b)
-            if (overlap(outs[a], outs[b])) return SSD_ERR_ALIAS;
-    }
+    const size_t nbk = tokens * d.ngroups * w->kn, nstk = (size_t)d.nseq * d.nheads * d.headdim * w->kn * 4;
+    const size_t nx = tokens * d.nheads * d.headdim;
+    w->B = align_up(w->inner.total, 256);
+    w->C = align_up(w->B + nbk * E, 256);
+    w->init = align_up(w->C + nbk * E, 256);
+    w->dfin = align_up(w->init + nstk, 256);
+    w->dinit = align_up(w->dfin + nstk, 256);
+    w->dB = align_up(w->dinit + nstk, 256);
+    w->dC = align_up(w->dB + nbk * 4, 256);
+    w->dx = align_up(w->dC + nbk * 4, 256);
+    w->ddt = align_up(w->dx + w->nsplit * align_up(nx * E, 256), 256);
+    w->dA = align_up(w->ddt + w->nsplit * align_up(tokens * d.nheads * 4, 256), 256);
+    w->dD = align_up(w->dA + (size_t)w->nsplit * d.nheads * 4, 256);
+    w->total = align_up(w->dD + (size_t)w->nsplit * d.nheads * 4, 256);
+    return true;
+}
 
-    char *ws = static_cast<char *>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = debug_check_cu_seqlens(cu_seqlens, d.nseq, d.seqlen, s);
-    if (st != SSD_OK) return st;
+size_t bwd_ws_total(const ssd_dims_t &d, ssd_dtype_t io, bool varlen) {
+    BwdSplitWs sw{};
+    bwd_split_ws(d, io, varlen, &sw);
+    return sw.nsplit > 1 ? sw.total : sw.inner.total;
+}
+
+// Runs the backward kernels on contiguous inputs whose state dim d.dstate is
+// built (validation done by the caller).
+ssd_status_t bwd_run(const ssd_dims_t &d, ssd_dtype_t io, const void *x, const float *dt, const float *A,
+                     const void *B, const void *C, const float *D, const float *init_state,
+                     const int32_t *cu_seqlens, const void *dy, const float *dfinal_state, void *dx, float *ddt,
+                     float *dA, float *dB, float *dC, float *dD, float *dinit_state, char *ws, hipStream_t s) {
+    BwdWs w{};
+    bwd_ws(d, cu_seqlens != nullptr, &w);
     ssd::BwdPrepParams pp{};
     pp.cu_seqlens = cu_seqlens;
     pp.batch = d.batch;
@@ -1145,6 +1156,149 @@ ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const vo
                         : ssd::bwd_dispatch<float>(kh.P, d.dstate, p, units, (unsigned)w.max_chunks, true, s);
     if (!ok) return SSD_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(ssd::ssd_bwd_reduce_kernel, dim3(d.nheads), dim3(256), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+// Columns [c0, c0 + w) of `rows` rows of `pitch_src` bytes into a packed
+// buffer (or back, with the pitches exchanged).
+bool copy_cols(void *dst, size_t dpitch, const void *src, size_t spitch, size_t width, size_t rows, hipStream_t s) {
+    if (rows == 0) return true;
+    return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, rows, hipMemcpyDeviceToDevice, s) == hipSuccess;
+}
+}  // namespace
+}  // extern "C"
+
+namespace ssd {
+// Sums of the state-dim slices' terms, slice 0 first: dx (rounded once to the
+// io dtype), ddt and dA; dD is slice 0's (it does not depend on the state dim).
+template <typename IO>
+__global__ __launch_bounds__(256) void ssd_bwd_combine_kernel(IO *dx, const IO *dxk, size_t nx, size_t px,
+                                                              float *ddt, const float *ddtk, size_t nt, size_t pt,
+                                                              float *dA, const float *dAk, float *dD,
+                                                              const float *dDk, int H, int nsplit) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nx; i += stride) {
+        float v = 0.f;
+        for (int k = 0; k < nsplit; ++k) v += to_f32(dxk[k * px + i]);
+        dx[i] = from_f32<IO>(v);
+    }
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nt; i += stride) {
+        float v = 0.f;
+        for (int k = 0; k < nsplit; ++k) v += ddtk[k * pt + i];
+        ddt[i] = v;
+    }
+    if (blockIdx.x == 0) {
+        for (int h = threadIdx.x; h < H; h += blockDim.x) {
+            float v = 0.f;
+            for (int k = 0; k < nsplit; ++k) v += dAk[k * H + h];
+            dA[h] = v;
+            dD[h] = dDk[h];
+        }
+    }
+}
+}  // namespace ssd
+
+extern "C" {
+
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims_t *dims, ssd_dtype_t io) {
+    if (!dims) return 0;
+    if (bwd_shape_check(dims, io, true) != SSD_OK && bwd_shape_check(dims, io, false) != SSD_OK) return 0;
+    const size_t a = bwd_ws_total(*dims, io, true), b = bwd_ws_total(*dims, io, false);
+    return a > b ? a : b;
+}
+
+ssd_status_t ssd_chunk_scan_bwd(const ssd_dims_t *dims, ssd_dtype_t io, const void *x, const float *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *init_state, const int32_t *cu_seqlens, const void *dy,
+                                const float *dfinal_state, void *dx, float *ddt, float *dA, float *dB, float *dC,
+                                float *dD, float *dinit_state, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    const bool varlen = cu_seqlens != nullptr;
+    ssd_status_t st = bwd_shape_check(dims, io, varlen);
+    if (st != SSD_OK) return st;
+    const ssd_dims_t &d = *dims;
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !dD) return SSD_ERR_NULL_PTR;
+    if (!workspace) return SSD_ERR_WORKSPACE;
+    const void *al16[] = {x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA, dB, dC, dD, dinit_state};
+    for (const void *q : al16)
+        if (q && !aligned(q, 16)) return SSD_ERR_ALIGNMENT;
+    if (!aligned(workspace, 256)) return SSD_ERR_ALIGNMENT;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
+    const size_t ws_total = bwd_ws_total(d, io, varlen);
+    if (workspace_bytes < ws_total) return SSD_ERR_WORKSPACE;
+
+    const size_t E = (io == SSD_BF16) ? 2 : 4;
+    const size_t tokens = (size_t)d.batch * d.seqlen;
+    const size_t nx = tokens * d.nheads * d.headdim, nbc = tokens * d.ngroups * d.dstate;
+    const size_t nst = (size_t)d.nseq * d.nheads * d.headdim * d.dstate * 4;
+    const Range ins[] = {rng(x, nx * E), rng(dt, tokens * d.nheads * 4), rng(A, (size_t)d.nheads * 4),
+                         rng(B, nbc * E), rng(C, nbc * E), rng(D, D ? (size_t)d.nheads * 4 : 0),
+                         rng(init_state, init_state ? nst : 0), rng(dy, nx * E),
+                         rng(dfinal_state, dfinal_state ? nst : 0),
+                         rng(cu_seqlens, varlen ? (size_t)(d.nseq + 1) * 4 : 0), rng(workspace, ws_total)};
+    const Range outs[] = {rng(dx, nx * E), rng(ddt, tokens * d.nheads * 4), rng(dA, (size_t)d.nheads * 4),
+                          rng(dB, nbc * 4), rng(dC, nbc * 4), rng(dD, (size_t)d.nheads * 4),
+                          rng(dinit_state, dinit_state ? nst : 0)};
+    for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+        for (const Range &r : ins)
+            if (overlap(outs[a], r)) return SSD_ERR_ALIAS;
+        for (size_t b = a + 1; b < sizeof(outs) / sizeof(outs[0]); ++b)
+            if (overlap(outs[a], outs[b])) return SSD_ERR_ALIAS;
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu_seqlens(cu_seqlens, d.nseq, d.seqlen, s);
+    if (st != SSD_OK) return st;
+    BwdSplitWs sw{};
+    bwd_split_ws(d, io, varlen, &sw);
+    if (sw.nsplit <= 1)
+        return bwd_run(d, io, x, dt, A, B, C, D, init_state, cu_seqlens, dy, dfinal_state, dx, ddt, dA, dB, dC, dD,
+                       dinit_state, ws, s);
+
+    // state-dim slices of kn columns: copy the slice's B, C and states in,
+    // run, copy its dB, dC and dinit columns out; dx, ddt and dA are summed
+    ssd_dims_t dk = d;
+    dk.dstate = sw.kn;
+    const size_t kn = (size_t)sw.kn, N = (size_t)d.dstate;
+    const size_t rows_bc = tokens * d.ngroups, rows_st = (size_t)d.nseq * d.nheads * d.headdim;
+    const size_t px = align_up(nx * E, 256), pt = align_up(tokens * d.nheads * 4, 256);
+    void *Bk = ws + sw.B, *Ck = ws + sw.C;
+    float *ik = init_state ? reinterpret_cast<float *>(ws + sw.init) : nullptr;
+    float *fk = dfinal_state ? reinterpret_cast<float *>(ws + sw.dfin) : nullptr;
+    float *dik = dinit_state ? reinterpret_cast<float *>(ws + sw.dinit) : nullptr;
+    float *dBk = reinterpret_cast<float *>(ws + sw.dB), *dCk = reinterpret_cast<float *>(ws + sw.dC);
+    for (int k = 0; k < sw.nsplit; ++k) {
+        const size_t c0 = (size_t)k * kn;
+        bool ok = copy_cols(Bk, kn * E, static_cast<const char *>(B) + c0 * E, N * E, kn * E, rows_bc, s) &&
+                  copy_cols(Ck, kn * E, static_cast<const char *>(C) + c0 * E, N * E, kn * E, rows_bc, s);
+        if (ik) ok = ok && copy_cols(ik, kn * 4, init_state + c0, N * 4, kn * 4, rows_st, s);
+        if (fk) ok = ok && copy_cols(fk, kn * 4, dfinal_state + c0, N * 4, kn * 4, rows_st, s);
+        if (!ok) return SSD_ERR_HIP;
+        st = bwd_run(dk, io, x, dt, A, Bk, Ck, k == 0 ? D : nullptr, ik, cu_seqlens, dy, fk, ws + sw.dx + k * px,
+                     reinterpret_cast<float *>(ws + sw.ddt + k * pt), reinterpret_cast<float *>(ws + sw.dA) + k * d.nheads,
+                     dBk, dCk, reinterpret_cast<float *>(ws + sw.dD) + k * d.nheads, dik, ws, s);
+        if (st != SSD_OK) return st;
+        ok = copy_cols(dB + c0, N * 4, dBk, kn * 4, kn * 4, rows_bc, s) &&
+             copy_cols(dC + c0, N * 4, dCk, kn * 4, kn * 4, rows_bc, s);
+        if (dik) ok = ok && copy_cols(dinit_state + c0, N * 4, dik, kn * 4, kn * 4, rows_st, s);
+        if (!ok) return SSD_ERR_HIP;
+    }
+    const size_t blocks = (nx + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
+    if (io == SSD_BF16)
+        hipLaunchKernelGGL(ssd::ssd_bwd_combine_kernel<ssd::bf16>, dim3(grid), dim3(256), 0, s,
+                           static_cast<ssd::bf16 *>(dx), reinterpret_cast<const ssd::bf16 *>(ws + sw.dx), nx,
+                           px / E, ddt, reinterpret_cast<const float *>(ws + sw.ddt), tokens * d.nheads, pt / 4, dA,
+                           reinterpret_cast<const float *>(ws + sw.dA), dD,
+                           reinterpret_cast<const float *>(ws + sw.dD), d.nheads, sw.nsplit);
+    else
+        hipLaunchKernelGGL(ssd::ssd_bwd_combine_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<float *>(dx),
+                           reinterpret_cast<const float *>(ws + sw.dx), nx, px / E, ddt,
+                           reinterpret_cast<const float *>(ws + sw.ddt), tokens * d.nheads, pt / 4, dA,
+                           reinterpret_cast<const float *>(ws + sw.dA), dD,
+                           reinterpret_cast<const float *>(ws + sw.dD), d.nheads, sw.nsplit);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }

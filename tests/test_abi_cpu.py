@@ -251,16 +251,21 @@ def test_bwd_workspace_size_query(lib):
     assert n128 >= 2 * 2 * 8 * 8 * 128 * 128 * 4 and n128 % 256 == 0
     assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(headdim=128, dstate=64)), ssd.SSD_F32) > 0
     assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(headdim=48)), ssd.SSD_BF16) == 0
-    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=256)), ssd.SSD_BF16) == 0
-    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=128)), ssd.SSD_F32) == 0
-    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=64)), ssd.SSD_F32) > 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=48)), ssd.SSD_BF16) == 0
+    # state dims beyond the kernels' (bf16 256, fp32 128 and 256) run in slices
+    # of the state dim: the workspace also holds the slices' inputs and terms
+    n64 = lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=64)), ssd.SSD_F32)
+    n128 = lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=128)), ssd.SSD_F32)
+    assert n64 > 0 and n128 > n64
+    for io, N in ((ssd.SSD_BF16, 256), (ssd.SSD_F32, 256)):
+        assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=N)), io) > 0
 
 
 @pytest.mark.parametrize("case,expect", [
     (dict(dims=None), 1),
     (dict(io=7), 3),
     (dict(dims=_dims(headdim=48)), 4),
-    (dict(dims=_dims(dstate=256)), 4),
+    (dict(dims=_dims(dstate=48)), 4),
     (dict(dims=_dims(nseq=3)), 2),
     (dict(dy=None), 1),
     (dict(dB=None), 1),

@@ -62,6 +62,12 @@ def _ref(inp, unit_mask=None):
     ("bf16", 1, 200, 4, 128, 64, 2, [64, 0, 1, 100, 35]),
     ("f32", 1, 150, 2, 128, 64, 1, None),
     ("f32", 1, 90, 4, 128, 32, 2, [30, 60]),
+    # state dims beyond the kernels' (bf16 256, fp32 128 and 256): one run per
+    # slice of the state dim, the slices' dx, ddt and dA terms summed
+    ("bf16", 2, 200, 4, 64, 256, 1, None),
+    ("bf16", 1, 200, 4, 128, 256, 2, [64, 0, 1, 100, 35]),
+    ("f32", 1, 150, 2, 64, 128, 1, None),
+    ("f32", 1, 90, 4, 32, 256, 2, [30, 60]),
 ])
 def test_backward_small(io, b, L, H, P, N, G, lengths):
     inp = _inputs(io, b, L, H, P, N, G, seed=L + H + N, lengths=lengths)
