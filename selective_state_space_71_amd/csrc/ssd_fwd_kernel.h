@@ -489,11 +489,12 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         const IO *Cg = reinterpret_cast<const IO *>(prm.C) + tok0 * bs + g * N;
 
         // ---- every global load of the item's set-up, issued together ----
-        // The first head's x and dt, the chunk's B rows, its C rows (for the
-        // read-out, when they go to LDS) and the C rows of this wave's tiles,
-        // as branch-free buffer loads (rows past the chunk lie past the
-        // buffers' end and read 0): one memory round trip, and each group is
-        // waited for only where it is used.
+        // The first head's x and dt, the chunk's B rows and the C rows of
+        // this wave's tiles (which, over the eight waves, are every row of the
+        // chunk: they also fill the C tile of the read-out), as branch-free
+        // buffer loads (rows past the chunk lie past the buffers' end and read
+        // 0): one memory round trip, and each group is waited for only where
+        // it is used.
         Prefetch<IO, P, N, Q> pf;
         pf.load(prm, tok0, q, h_begin, tid, wave, true);
         constexpr int VPR = S::NP * S::E / 16;   // 16-byte vectors per padded row
@@ -516,11 +517,6 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         i32x4 bv[NV];
     #pragma unroll
         for (int k = 0; k < NV; ++k) bv[k] = __builtin_amdgcn_raw_buffer_load_b128(rB, row_vec_off(k), 0, 0);
-        i32x4 cv[S::kCInLds ? NV : 1];
-        if constexpr (S::kCInLds) {
-    #pragma unroll
-            for (int k = 0; k < NV; ++k) cv[k] = __builtin_amdgcn_raw_buffer_load_b128(rC, row_vec_off(k), 0, 0);
-        }
 
         // ---- this wave's row tiles, their C rows and their C B^T tiles ----
         // Tile Ia = wave; tile Ib = 2*kWaves-1-wave when the chunk has 2*kWaves
@@ -608,15 +604,18 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             }
         }
         // With the B^T operands in registers, the B chunk is dead: its LDS then
-        // holds the chunk's C rows for the read-out (row layout, like B).
+        // holds the chunk's C rows for the read-out (row layout, like B),
+        // written from the C fragments of the waves' row tiles (tiles w and
+        // 2 kWaves - 1 - w cover the chunk; rows past it hold zeros).
         IO *sC = sB;
         if constexpr (S::kBtRegs) {
             __syncthreads();   // every wave is done with the B chunk
             if constexpr (S::kCInLds) {
     #pragma unroll
-                for (int k = 0; k < NV; ++k) {
-                    int j, c;
-                    if (row_vec(k, j, c)) *reinterpret_cast<i32x4 *>(sC + lds_off<IO, S::NP>(j, c * (16 / S::E))) = cv[k];
+                for (int ks = 0; ks < S::NK; ++ks) {
+                    const int col = ks * 32 + 8 * lg;
+                    if (Ia < S::QT) *reinterpret_cast<Frag *>(sC + lds_off<IO, S::NP>(16 * Ia + li, col)) = cga[ks];
+                    if (S::kTwoTiles) *reinterpret_cast<Frag *>(sC + lds_off<IO, S::NP>(16 * Ib + li, col)) = cgb[ks];
                 }
             }
             // (read only after the first head's staging barrier)
