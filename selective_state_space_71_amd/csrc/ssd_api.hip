@@ -70,49 +70,85 @@ struct PrepParams {
 __device__ bool build_packed_schedule(const PrepParams &p) {
     const int tid = threadIdx.x;
     const int Q = p.Q;
-    __shared__ int s_valid;
+    const int n = p.nseq;
+    // Offsets and chunk starts of up to kCache sequences are read from LDS
+    // (the loops below would otherwise wait on one global load per step).
+    constexpr int kCache = 4096;
+    __shared__ int s_cu[kCache + 1], s_cs[kCache + 1];
+    __shared__ long long s_part[256];
+    __shared__ int s_bad;
+    const bool cached = n <= kCache;
+    if (tid == 0) s_bad = 0;
+    if (cached)
+        for (int i = tid; i <= n; i += 256) s_cu[i] = p.cu_seqlens[i];
+    __syncthreads();
+    auto cu = [&](int i) { return cached ? s_cu[i] : p.cu_seqlens[i]; };
+    // every thread checks and counts the chunks of a contiguous block of
+    // sequences; then the block counts are prefix-summed
+    const int per = (n + 255) / 256;
+    const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
+    long long cnt = 0;
+    bool bad = tid == 0 && !(cu(0) == 0 && cu(n) == p.seqlen);
+    for (int s = s0; s < s1; ++s) {
+        const int a = cu(s), e = cu(s + 1);
+        bad = bad || !(a >= 0 && e >= a && e <= p.seqlen);
+        cnt += (e > a) ? ((long long)e - a + Q - 1) / Q : 0;
+    }
+    s_part[tid] = cnt;
+    if (bad) atomicOr(&s_bad, 1);
+    __syncthreads();
     if (tid == 0) {
         long long acc = 0;
-        bool ok = p.cu_seqlens[0] == 0 && p.cu_seqlens[p.nseq] == p.seqlen;
-        for (int s = 0; s < p.nseq && ok; ++s) {
-            const int a = p.cu_seqlens[s], e = p.cu_seqlens[s + 1];
-            ok = a >= 0 && e >= a && e <= p.seqlen;
-            p.seq_chunk_start[s] = (int)acc;
-            acc += (e > a) ? (e - a + Q - 1) / Q : 0;
-            ok = ok && acc <= p.max_entries;
+        for (int t = 0; t < 256; ++t) {
+            const long long v = s_part[t];
+            s_part[t] = acc;
+            acc += v;
         }
+        const bool ok = !s_bad && acc <= p.max_entries;
         if (!ok) {
             *p.error |= 2;
             acc = 0;
+            s_bad = 1;
         }
-        p.seq_chunk_start[p.nseq] = (int)acc;
+        p.seq_chunk_start[n] = (int)acc;
+        if (cached) s_cs[n] = (int)acc;
         *p.n_chunks = (int)acc;
-        s_valid = ok ? 1 : 0;
     }
     __syncthreads();
-    if (!s_valid) return false;
-    const int total = p.seq_chunk_start[p.nseq];
+    if (s_bad) return false;
+    {
+        long long acc = s_part[tid];
+        for (int s = s0; s < s1; ++s) {
+            const int a = cu(s), e = cu(s + 1);
+            p.seq_chunk_start[s] = (int)acc;
+            if (cached) s_cs[s] = (int)acc;
+            acc += (e > a) ? ((long long)e - a + Q - 1) / Q : 0;
+        }
+    }
+    __syncthreads();
+    auto cs = [&](int i) { return cached ? s_cs[i] : p.seq_chunk_start[i]; };
+    const int total = cs(n);
     for (int f = tid; f < total; f += 256) {
-        int lo = 0, hi = p.nseq - 1;  // last s with seq_chunk_start[s] <= f
+        int lo = 0, hi = n - 1;  // last s with seq_chunk_start[s] <= f
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (p.seq_chunk_start[mid] <= f) lo = mid; else hi = mid - 1;
+            if (cs(mid) <= f) lo = mid; else hi = mid - 1;
         }
         const int s = lo;
-        const int c = f - p.seq_chunk_start[s];
+        const int c = f - cs(s);
         // position in chunk-index-major order
         int idx = 0;
-        for (int t = 0; t < p.nseq; ++t) {
-            const int nct = p.seq_chunk_start[t + 1] - p.seq_chunk_start[t];
+        for (int t = 0; t < n; ++t) {
+            const int nct = cs(t + 1) - cs(t);
             idx += min(nct, c) + ((t < s && nct > c) ? 1 : 0);
         }
-        const int start = p.cu_seqlens[s] + c * Q;
-        const int len = min(Q, p.cu_seqlens[s + 1] - start);
+        const int start = cu(s) + c * Q;
+        const int len = min(Q, cu(s + 1) - start);
         p.chunks[idx] = make_int4(s, c, start, len);
     }
     if (p.final_state) {
-        for (int s = 0; s < p.nseq; ++s) {
-            if (p.cu_seqlens[s + 1] > p.cu_seqlens[s]) continue;
+        for (int s = 0; s < n; ++s) {
+            if (cu(s + 1) > cu(s)) continue;
             const long long base = (long long)s * p.H * p.state_elems;
             for (long long k = tid; k < (long long)p.H * p.state_elems; k += 256)
                 p.final_state[base + k] = p.init_state ? p.init_state[base + k] : 0.f;
