@@ -1,9 +1,10 @@
 """Seeded randomized parity against the fp64 oracle: a fixed draw of shapes
 (head and state dims, chunk lengths, groups, dense and packed batches, initial
 states, both io dtypes) through the forward, the backward, the decode step and
-the block prologue and epilogue.  Same tolerances as the other GPU tests; dA,
-a sum over every token whose terms can cancel, is held to 64 ulps of its term
-scale (the oracle's dA_abs) where that is the looser bound.
+the block prologue and epilogue.  Same tolerances as the other GPU tests; dA
+and dD, sums over every token whose terms can cancel, are held to 64 ulps of
+their term scales (the oracle's dA_abs; the sum of |dy x|) where that is the
+looser bound.
 """
 import numpy as np
 import pytest
@@ -62,12 +63,17 @@ def test_random_forward_and_backward(seed):
         # the backward of every forward shape (state dims beyond its kernels run in slices)
         binp = _inputs(io, b, L, H, P, N, G, seed=int(rng.integers(1 << 30)), lengths=lens, init=init)
         got, ref = _gpu(binp), _ref(binp)
+        # dA and dD are sums over every token whose terms can cancel: where the
+        # relative bar is the tighter one they are held to 64 ulps of their
+        # term scales (dA: the oracle's dA_abs; dD = sum dy.x: sum |dy x|)
+        dD_abs = np.abs(wl.as_f64(binp["dy"], io) * wl.as_f64(binp["x"], io)).sum(axis=(0, 1, 3))
+        scale = {"dA": ref["dA_abs"], "dD": dD_abs}
         for k in GRADS:
             g = hp.to_numpy64(got[k])
             if hp.rel_l2(g, ref[k]) <= hp.TOL[io]:
                 continue
-            assert k == "dA", (tag, k, hp.rel_l2(g, ref[k]))
-            assert np.all(np.abs(g - ref[k]) <= 64 * EPS[io] * ref["dA_abs"]), (tag, g, ref[k])
+            assert k in scale, (tag, k, hp.rel_l2(g, ref[k]))
+            assert np.all(np.abs(g - ref[k]) <= 64 * EPS[io] * scale[k]), (tag, k, g, ref[k])
 
 
 @pytest.mark.parametrize("seed", range(2))
