@@ -930,7 +930,9 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
         for (int k = 0; k < UV; ++k) {
             const int i = tid + 256 * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
             ur[k] = zero_frag<bf16x8>();
-            if (j < q) ur[k] = *reinterpret_cast<const bf16x8 *>(ug + ((t0 + j) * p.H + h) * P + c8);
+            // (non-temporal: the head's rows are read once here, and the L2 keeps
+            // the chunk's B or C rows that the group's other heads read too)
+            if (j < q) ur[k] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(ug + ((t0 + j) * p.H + h) * P + c8));
         }
 #pragma unroll
         for (int k = 0; k < VV; ++k) {
