@@ -334,9 +334,9 @@ struct Prefetch {
     // Unit u covers tokens 4*t4 .. 4*t4+3 and channels p0 .. p0+7.  With 64
     // channels (eight blocks), the eight lanes of a run take the eight blocks
     // of one token group, so a wave's load instruction reads whole 128-byte
-    // rows of x (non-temporal: each row is read once); lane bit 3 and lane bits 4-5 pick the token group, which with
-    // x_lds_off's swizzle keeps the 8-byte staging writes of 32 lanes on
-    // distinct banks.  Other widths: sixteen consecutive units take sixteen
+    // rows of x (non-temporal: each row is read once); lane bit 3 and lane
+    // bits 4-5 pick the token group, which with x_lds_off's swizzle keeps the
+    // 8-byte staging writes of 32 lanes on distinct banks.  Other widths: sixteen consecutive units take sixteen
     // consecutive token groups of one channel block.
     static __device__ __forceinline__ int unit_t4(int u) {
         if constexpr (PB == 8) return 8 * (u >> 6) + 4 * ((u >> 3) & 1) + ((u >> 4) & 3);
