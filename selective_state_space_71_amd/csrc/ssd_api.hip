@@ -1098,6 +1098,11 @@ ssd_status_t bwd_shape_check(const ssd_dims_t *dims, ssd_dtype_t io, bool varlen
     if (bwd_kernel_n(d, io) == 0) return SSD_ERR_UNSUPPORTED;
     if ((long long)d.batch * d.seqlen > INT_MAX / 2 || (long long)d.nseq * kernel_heads(d).H > INT_MAX)
         return SSD_ERR_SHAPE;
+    // the scans address one chunk of x, dy, B or C rows (every head or group)
+    // with 32-bit byte offsets
+    if ((long long)d.nheads * d.headdim * ssd::kBwdQ * 4 >= (1LL << 30) ||
+        (long long)d.ngroups * d.dstate * ssd::kBwdQ * 4 >= (1LL << 30))
+        return SSD_ERR_SHAPE;
     return SSD_OK;
 }
 

@@ -864,11 +864,17 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
 // The two scans are independent, so one launch runs both (twice the
 // workgroups of either: the chains are latency-bound), and its register
 // budget allows three workgroups per compute unit.  The next chunk's rows
-// and dt are loaded into registers while the current chunk is computed; u is scaled by the decay weights once per chunk and kept in LDS
-// as a split bf16 pair, and both MFMA operands are read in the K-slot order
-// with transposing LDS reads.
-template <int P, int N>
-__global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
+// and dt are loaded into registers while the current chunk is computed; u is
+// scaled by the decay weights once per chunk and kept in LDS as a split bf16
+// pair, and both MFMA operands are read in the K-slot order with transposing
+// LDS reads.  Every global access goes through a buffer resource, rows past
+// the chunk (and a missing state) given as out-of-range offsets that read
+// zero, so that each path issues the same memory operations: the compiler
+// then waits for the prefetched rows alone, and the state stores, issued
+// after them, stay in flight while the next chunk is staged.
+template <int P, int N, int MODE>
+__device__ __forceinline__ void scan_bf16_chain(const BwdParams &p, int unit, bf16 *sv, bf16 *uh, bf16 *ul,
+                                                float *swt, float *salpha) {
     constexpr int Q = kBwdQ;
     constexpr int PT = P / 16, NT = N / 16, TILES = PT * NT;
     constexpr int TPW = (TILES + 3) / 4;
@@ -876,76 +882,88 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
     constexpr int UV = Q * P / 8 / 256;     // 16-byte pieces of u per thread (P >= 32: 1 or 2)
     constexpr int VV = Q * N / 8 / 256;     // likewise for v (1, 2 or 4)
     static_assert(UV >= 1 && VV >= 1, "shape too small for this kernel");
-    __shared__ __attribute__((aligned(16))) bf16 sv[Q * SN];
-    __shared__ __attribute__((aligned(16))) bf16 uh[Q * SP];
-    __shared__ __attribute__((aligned(16))) bf16 ul[Q * SP];
-    __shared__ float swt[Q];
-    __shared__ float salpha;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int PN = P * N;
+    // (wave masked to its 0..3 range: the tile tests below then fold away)
+    const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3;
     const int li = lane & 15, lg = lane >> 4;
-    // blocks [0, nseq H): forward boundary states (mode 0); [nseq H, 2 nseq H): the reverse chain (mode 1)
-    const int units = p.nseq * p.H;
-    const int mode = (int)blockIdx.x >= units;
-    const int unit = (int)blockIdx.x - mode * units;
     const int s = unit / p.H, h = unit - s * p.H;
     const int g = h / (p.H / p.G);
     const int o = p.seq_chunk_start[s];
     const int nc = p.seq_chunk_start[s + 1] - o;
-    const long long PN = (long long)P * N;
-    const bf16 *ug = reinterpret_cast<const bf16 *>(mode == 0 ? p.x : p.dy);
-    const bf16 *vg = reinterpret_cast<const bf16 *>(mode == 0 ? p.B : p.C);
+    const bf16 *ug = reinterpret_cast<const bf16 *>(MODE == 0 ? p.x : p.dy);
+    const bf16 *vg = reinterpret_cast<const bf16 *>(MODE == 0 ? p.B : p.C);
     const float Ah = p.A[h / p.hsub];
+    const int HP = p.H * P, GN = p.G * N, HD = p.H / p.hsub;   // row strides of u, v and dt
 
-    f32x4 st[TPW];
-    const float *st0 = mode == 0 ? p.init_state : p.dfinal;
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
+    // Wave w holds state tiles t = w + 4 k, (pt, nt) = (t % PT, t / PT):
+    // element r of tile k is state[pt*16 + li][nt*16 + 4 lg + r].
+    auto tile_off = [&](int k) {   // byte offset of this lane's 4 floats of tile k
         const int t = wave + 4 * k;
-        st[k] = zero4();
-        if (t < TILES && st0) {
-            const int pp = (t % PT) * 16 + li, nn = (t / PT) * 16 + 4 * lg;
-            st[k] = *reinterpret_cast<const f32x4 *>(st0 + ((long long)s * p.H + h) * PN + pp * N + nn);
-        }
-    }
-    auto store_state = [&](float *dst) {
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int t = wave + 4 * k;
-            if (t < TILES) {
-                const int pp = (t % PT) * 16 + li, nn = (t / PT) * 16 + 4 * lg;
-                *reinterpret_cast<f32x4 *>(dst + pp * N + nn) = st[k];
-            }
-        }
+        return ((t % PT) * 16 + li) * N * 4 + ((t / PT) * 16 + 4 * lg) * 4;
     };
-    if (mode == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
 
-    // registers of one chunk: u and v pieces (row j, 8 columns) and dt (wave 0)
+    // the sequence's chunks are consecutive Q-token pieces from its first token
+    long long seq_t0 = 0;
+    int seq_len = 0;
+    if (nc > 0) {
+        const int4 f = p.chunks[o], l = p.chunks[o + nc - 1];
+        seq_t0 = f.y;
+        seq_len = l.y + l.z - f.y;
+    }
+    // registers of one chunk: u and v pieces (row j, 8 columns) and dt; a
+    // chunk index outside the sequence loads zeros
     bf16x8 ur[UV], vr[VV];
-    float dtr = 0.f;
+    float dtr;
     auto load_chunk = [&](int c) {
-        const int4 ce = p.chunks[o + c];
-        const long long t0 = ce.y;
-        const int q = ce.z;
-#pragma unroll
-        for (int k = 0; k < UV; ++k) {
-            const int i = tid + 256 * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
-            ur[k] = zero_frag<bf16x8>();
-            // (non-temporal: the head's rows are read once here, and the L2 keeps
-            // the chunk's B or C rows that the group's other heads read too)
-            if (j < q) ur[k] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(ug + ((t0 + j) * p.H + h) * P + c8));
-        }
+        const bool in = c >= 0 && c < nc;
+        const int q = in ? min(Q, seq_len - c * Q) : 0;
+        const long long t0 = seq_t0 + (long long)(in ? c : 0) * Q;
+        // (u non-temporal: the head's rows are read once here, and the L2
+        // keeps the chunk's B or C rows that the group's other heads read too)
+        const __amdgpu_buffer_rsrc_t ru = buf_rsrc(ug + t0 * HP, q * HP * 2);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vg + t0 * GN, q * GN * 2);
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(p.dt + t0 * HD, q * HD * 4);
+        // issued in the order of first use (dt, v, u), the same on every
+        // path into the chunk loop, so that the waits at its top are exact
+        dtr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (lane * HD + h / p.hsub) * 4, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < VV; ++k) {
             const int i = tid + 256 * k, j = i / (N / 8), c8 = (i % (N / 8)) * 8;
-            vr[k] = zero_frag<bf16x8>();
-            if (j < q) vr[k] = *reinterpret_cast<const bf16x8 *>(vg + ((t0 + j) * p.G + g) * N + c8);
+            vr[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, (j * GN + g * N + c8) * 2, 0, 0));
         }
-        if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * (p.H / p.hsub) + h / p.hsub] : 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < UV; ++k) {
+            const int i = tid + 256 * k, j = i / (P / 8), c8 = (i % (P / 8)) * 8;
+            ur[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ru, (j * HP + h * P + c8) * 2, 0, kStream));
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
-    if (nc > 0) load_chunk(mode == 0 ? 0 : nc - 1);
+    load_chunk(MODE == 0 ? 0 : nc - 1);
+
+    f32x4 st[TPW];
+    {
+        const float *st0 = MODE == 0 ? p.init_state : p.dfinal;
+        const __amdgpu_buffer_rsrc_t r0 =
+            buf_rsrc(st0 ? st0 + ((long long)s * p.H + h) * PN : nullptr, st0 ? PN * 4 : 0);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k)
+            st[k] = wave + 4 * k < TILES
+                ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, tile_off(k), 0, 0))
+                : zero4();
+    }
+    auto store_state = [&](float *dst) {   // null: no store
+        const __amdgpu_buffer_rsrc_t r = buf_rsrc(dst, dst ? PN * 4 : 0);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k)
+            if (wave + 4 * k < TILES)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, st[k]), r, tile_off(k), 0, 0);
+    };
+    if (MODE == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
 
     for (int step = 0; step < nc; ++step) {
-        const int c = mode == 0 ? step : nc - 1 - step;
+        const int c = MODE == 0 ? step : nc - 1 - step;
         // v rows and the weights of this chunk into LDS
 #pragma unroll
         for (int k = 0; k < VV; ++k) {
@@ -953,10 +971,10 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
             *reinterpret_cast<bf16x8 *>(sv + j * SN + c8) = vr[k];
         }
         if (wave == 0) {
-            const float sc = wave_inclusive_sum(dtr * Ah) * kLog2e;
+            const float sc = wave_inclusive_sum(dtr * Ah) * kLog2e;   // s * log2(e)
             const float slast = __shfl(sc, 63, 64);
-            swt[lane] = mode == 0 ? __builtin_amdgcn_exp2f(slast - sc) * dtr : __builtin_amdgcn_exp2f(sc);
-            if (lane == 0) salpha = __builtin_amdgcn_exp2f(slast);
+            swt[lane] = MODE == 0 ? __builtin_amdgcn_exp2f(slast - sc) * dtr : __builtin_amdgcn_exp2f(sc);
+            if (lane == 0) *salpha = __builtin_amdgcn_exp2f(slast);
         }
         __syncthreads();
         // u scaled by the weights, as a split pair
@@ -974,10 +992,10 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
             *reinterpret_cast<bf16x8 *>(uh + j * SP + c8) = hi;
             *reinterpret_cast<bf16x8 *>(ul + j * SP + c8) = lo;
         }
-        const float alpha = salpha;
+        const float alpha = *salpha;
         __syncthreads();
-        if (step + 1 < nc) load_chunk(mode == 0 ? c + 1 : c - 1);   // in flight during the MFMAs
-        if (mode == 1) store_state(p.radj + ((long long)(o + c) * p.H + h) * PN);
+        load_chunk(MODE == 0 ? c + 1 : c - 1);   // in flight during the MFMAs (zeros past the end)
+        if (MODE == 1) store_state(p.radj + ((long long)(o + c) * p.H + h) * PN);
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
             const int t = wave + 4 * k;
@@ -995,10 +1013,27 @@ __global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) 
                 for (int r = 0; r < 4; ++r) st[k][r] = alpha * st[k][r] + acc[r];
             }
         }
-        if (mode == 0) store_state(p.states + ((long long)(o + s + c + 1) * p.H + h) * PN);
+        if (MODE == 0) store_state(p.states + ((long long)(o + s + c + 1) * p.H + h) * PN);
         __syncthreads();   // the LDS tiles are rewritten by the next chunk
     }
-    if (mode == 1 && p.dinit) store_state(p.dinit + ((long long)s * p.H + h) * PN);
+    if (MODE == 1) store_state(p.dinit ? p.dinit + ((long long)s * p.H + h) * PN : nullptr);
+}
+
+// Blocks [0, nseq H) run the forward boundary states (MODE 0), blocks
+// [nseq H, 2 nseq H) the reverse chain (MODE 1).
+template <int P, int N>
+__global__ __launch_bounds__(256, 3) void ssd_bwd_scan_bf16_kernel(BwdParams p) {
+    constexpr int Q = kBwdQ;
+    __shared__ __attribute__((aligned(16))) bf16 sv[Q * (N + 8)];
+    __shared__ __attribute__((aligned(16))) bf16 uh[Q * (P + 8)];
+    __shared__ __attribute__((aligned(16))) bf16 ul[Q * (P + 8)];
+    __shared__ float swt[Q];
+    __shared__ float salpha;
+    const int units = p.nseq * p.H;
+    if ((int)blockIdx.x < units)
+        scan_bf16_chain<P, N, 0>(p, blockIdx.x, sv, uh, ul, swt, &salpha);
+    else
+        scan_bf16_chain<P, N, 1>(p, (int)blockIdx.x - units, sv, uh, ul, swt, &salpha);
 }
 
 // dA[h], dD[h]: sums of the per-chunk partials of the model head's kernel

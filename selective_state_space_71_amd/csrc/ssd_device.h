@@ -25,6 +25,8 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Io;
 
@@ -52,6 +54,23 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// Buffer resource over `bytes` bytes at `base`: reads past the end return 0
+// and writes past it are dropped (0 bytes: every access is a no-op).  The
+// kernels' loops make their global accesses through these, with out-of-range
+// offsets instead of branches, so that every path issues the same vector
+// memory operations: the compiler then knows how many follow each load and
+// waits for exactly the ones a use needs (operations issued under a branch
+// make it wait for whatever might have been issued).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+// Cache-policy operand of a buffer access that streams data used once (a
+// head's x or dy rows, the y rows): non-temporal, so that these lines are
+// the first the XCD's L2 gives up and the data that is read again (states
+// handed from chunk to chunk, the B and C rows a group's heads share) stays.
+constexpr int kStream = 2;   // nt
 
 template <typename Frag> __device__ __forceinline__ Frag zero_frag() {
     Frag f;

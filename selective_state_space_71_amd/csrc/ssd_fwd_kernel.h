@@ -186,9 +186,6 @@ struct FwdShape {
                                   Q % BLK == 0;
 };
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
 // K-slot order.  Every contraction over chunk tokens uses the same slot
 // order: within a 32-token K step, slot e (0..7) of lane group lg holds token
 //     16 * (e / 4) + 4 * lg + e % 4,
@@ -222,28 +219,12 @@ __device__ __forceinline__ int lds_off(int row, int col) {
     }
 }
 
-// Buffer resource over `bytes` bytes at `base`: reads past the end return 0
-// and writes past it are dropped (0 bytes: every access is a no-op).  The
-// head loop makes its global accesses through these, with out-of-range
-// offsets instead of branches, so that every path issues the same vector
-// memory operations: the compiler then knows how many follow each load and
-// waits for exactly the ones a use needs (operations issued under a branch
-// make it wait for whatever might have been issued).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
 constexpr int kPastEnd = 0x40000000;   // a byte offset beyond every buffer of the kernel
 
 // s_waitcnt operand that waits until at most n vector memory operations are
 // outstanding (and for nothing else): vmcnt in bits 3:0 and 15:14, expcnt (7)
 // and lgkmcnt (15) at their no-wait maxima.
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Cache-policy operand of a buffer access that streams data used once (the x
-// rows of a head, the y rows): non-temporal, so that these lines are the
-// first the XCD's L2 gives up and the boundary states handed from chunk to
-// chunk stay there.
-constexpr int kStream = 2;   // nt
 
 template <typename IO, int AUX = 0>
 __device__ __forceinline__ typename Io<IO>::Frag buf_load_frag(__amdgpu_buffer_rsrc_t r, int off) {
