@@ -52,6 +52,8 @@ struct BwdParams {
     // workspace
     const int4 *chunks;           // [n_chunks] {seq, first token, length, chunk index in seq}
     const int *seq_chunk_start;   // [nseq + 1]
+    // (each P x N state row-major, or in state_piece_pos's tile order where
+    // the bf16 scans write it for the bf16 chunk kernel)
     float *states;                // [n_chunks + nseq][H][P][N]: H_0 .. H_T of every sequence
     float *radj;                  // [n_chunks][H][P][N]: R_c
     float *partA, *partD;         // [n_chunks][H]
@@ -513,6 +515,21 @@ __device__ __forceinline__ f32x4 mfma_bf16(f32x4 acc, bf16x8 a, bf16x8 b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+// Order of the chunk states H_c and R_c in the workspace, shared by the
+// bf16 scans (writers) and the bf16 chunk kernel (reader): the 16 x 16
+// tiles t = pt + (P / 16) nt in turn, each as 64 pieces of 4 floats in the
+// lane order of the MFMA accumulator, piece l holding
+// state[16 pt + l % 16][16 nt + 4 (l / 16) + 0..3].  A wave's store of one
+// tile is then 1 KB of consecutive bytes (in row-major order it is 16 half
+// lines).
+template <int P>
+__device__ __forceinline__ void state_piece_pos(int piece, int &pp, int &nn) {
+    constexpr int PT = P / 16;
+    const int t = piece >> 6, l = piece & 63;
+    pp = (t % PT) * 16 + (l & 15);
+    nn = (t / PT) * 16 + 4 * (l >> 4);
+}
+
 constexpr int kBwdChunkWaves = 8;   // waves per workgroup of the bf16 chunk kernel (4 or 8)
 
 template <int P, int N, int NW>
@@ -646,9 +663,9 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         float hrd = 0.f;   // <R_c, H_c>
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
-            const int i = (tid + NTH * k) * 4;
-            if (i >= 4 * SP4) break;
-            const int pp = i / N, nn = i - pp * N;
+            if (tid + NTH * k >= SP4) break;
+            int pp, nn;
+            state_piece_pos<P>(tid + NTH * k, pp, nn);
             bf16x4 a, b, cc, d;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -897,7 +914,7 @@ __device__ __forceinline__ void scan_bf16_chain(const BwdParams &p, int unit, bf
 
     // Wave w holds state tiles t = w + 4 k, (pt, nt) = (t % PT, t / PT):
     // element r of tile k is state[pt*16 + li][nt*16 + 4 lg + r].
-    auto tile_off = [&](int k) {   // byte offset of this lane's 4 floats of tile k
+    auto tile_off = [&](int k) {   // byte offset of this lane's 4 floats of tile k, row-major state
         const int t = wave + 4 * k;
         return ((t % PT) * 16 + li) * N * 4 + ((t / PT) * 16 + 4 * lg) * 4;
     };
@@ -953,12 +970,15 @@ __device__ __forceinline__ void scan_bf16_chain(const BwdParams &p, int unit, bf
                 ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, tile_off(k), 0, 0))
                 : zero4();
     }
-    auto store_state = [&](float *dst) {   // null: no store
+    // the workspace's states in the tile order of state_piece_pos (tile t, this
+    // lane's piece); the initial-state gradient row-major (null: no store)
+    auto store_state = [&](float *dst, bool row_major = false) {
         const __amdgpu_buffer_rsrc_t r = buf_rsrc(dst, dst ? PN * 4 : 0);
 #pragma unroll
         for (int k = 0; k < TPW; ++k)
             if (wave + 4 * k < TILES)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, st[k]), r, tile_off(k), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, st[k]), r,
+                                                       row_major ? tile_off(k) : ((wave + 4 * k) * 64 + lane) * 16, 0, 0);
     };
     if (MODE == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
 
@@ -1016,7 +1036,7 @@ __device__ __forceinline__ void scan_bf16_chain(const BwdParams &p, int unit, bf
         if (MODE == 0) store_state(p.states + ((long long)(o + s + c + 1) * p.H + h) * PN);
         __syncthreads();   // the LDS tiles are rewritten by the next chunk
     }
-    if (MODE == 1) store_state(p.dinit ? p.dinit + ((long long)s * p.H + h) * PN : nullptr);
+    if (MODE == 1) store_state(p.dinit ? p.dinit + ((long long)s * p.H + h) * PN : nullptr, true);
 }
 
 // Blocks [0, nseq H) run the forward boundary states (MODE 0), blocks
