@@ -553,6 +553,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
     __shared__ __attribute__((aligned(16))) bf16 Hl[P * SN];
     __shared__ __attribute__((aligned(16))) bf16 Rh[P * SN];
     __shared__ __attribute__((aligned(16))) bf16 Rl[P * SN];
+    __shared__ __attribute__((aligned(16))) bf16 dxs[Q * SP];   // a head's dx rows, written out a head later
     __shared__ float s2[Q], dtv[Q], ew[Q], es[Q];
     __shared__ float rowP[NH][Q], colP[4][Q], offBP[NH][Q], offCP[NH][Q];
     __shared__ float red[NW], hrp[NW];
@@ -569,6 +570,17 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
     const int H = p.H, hpg = H / p.G;
     const long long PN = (long long)P * N;
     const bf16 *xg = reinterpret_cast<const bf16 *>(p.x), *dyg = reinterpret_cast<const bf16 *>(p.dy);
+    bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
+    // dx rows of head hp from LDS, as whole 128-byte rows (the dx phase's
+    // lanes hold 8-byte pieces of 16 tokens)
+    auto flush_dx = [&](int hp) {
+        for (int i = threadIdx.x; i < Q * (P / 8); i += NTH) {
+            const int j = i / (P / 8), c8 = (i % (P / 8)) * 8;
+            if (j < q)
+                *reinterpret_cast<bf16x8 *>(dxg + ((t0 + j) * H + hp) * P + c8) =
+                    *reinterpret_cast<const bf16x8 *>(dxs + j * SP + c8);
+        }
+    };
 
     // B and C rows of the chunk (once per group)
     for (int i = tid; i < Q * (N / 8); i += NTH) {
@@ -648,6 +660,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         asm volatile("" : "+v"(tid_));
         const int tid = tid_, lane = tid & 63, li = lane & 15, lg = lane >> 4;
         __syncthreads();   // the previous head's tiles are no longer read
+        if (hh > 0) flush_dx(h - 1);
         // this head's registers into LDS; dy . x over the chunk from the same registers
         float dd = 0.f;
 #pragma unroll
@@ -744,10 +757,9 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         if (hh + 1 < hpg) load_r(h + 1);
         // dx = M^T dY + diag(w) B R^T + D dY (this band, this half's columns)
         const float Dh = p.D ? p.D[h / p.hsub] : 0.f;
-        bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
         // computed transposed (rows head-dim, columns tokens), so that each lane
         // holds 4 consecutive head-dim entries of one token: one 8-byte dy read
-        // and one 8-byte store per tile
+        // and one 8-byte piece of the LDS dx rows per tile
 #pragma unroll
         for (int u = 0; u < PT2; ++u) {
             const int pt = half * PT2 + u;
@@ -765,7 +777,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
                 bf16x4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = (bf16)(a1[r] + wj * a2[r] + Dh * (float)dyv[r]);
-                *reinterpret_cast<bf16x4 *>(dxg + ((t0 + j) * H + h) * P + p0) = o;
+                *reinterpret_cast<bf16x4 *>(dxs + j * SP + p0) = o;
             }
         }
 
@@ -835,6 +847,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
     // diagonal parts of dB and dC: (sum_h W_h)^T C and (sum_h W_h) B, with the
     // sum as a split bf16 pair (high parts in Ms, remainders in Ws)
     __syncthreads();   // every wave is done with the last head's tiles
+    if (hpg > 0) flush_dx(g * hpg + hpg - 1);
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
         const int j = (JT * half + u) * 16 + li;
