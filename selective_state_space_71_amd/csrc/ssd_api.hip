@@ -144,7 +144,7 @@ __device__ bool build_packed_schedule(const PrepParams &p) {
         }
         const int start = cu(s) + c * Q;
         const int len = min(Q, cu(s + 1) - start);
-        p.chunks[idx] = make_int4(s, c, start, len);
+        p.chunks[idx] = make_int4(s, c, start, len | (start + len == cu(s + 1) ? ssd::kLastChunk : 0));
     }
     if (p.final_state) {
         for (int s = 0; s < n; ++s) {
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams p) {
             const int s = e - c * p.batch;
             const int start = c * Q;
             const int len = min(Q, p.seqlen - start);
-            p.chunks[e] = make_int4(s, c, s * p.seqlen + start, len);
+            p.chunks[e] = make_int4(s, c, s * p.seqlen + start, len | (c == nc - 1 ? ssd::kLastChunk : 0));
         }
     } else {
         build_packed_schedule(p);   // an invalid table leaves zero entries

@@ -83,6 +83,20 @@ __device__ __forceinline__ void race_widen_delay(int unit, int cloc, int wave) {
     for (int k = 0; k < n; ++k) __builtin_amdgcn_s_sleep(8);
 }
 
+// Mark in a chunk entry's length field: the sequence's last chunk, whose
+// boundary state is the final state.
+constexpr int kLastChunk = 1 << 30;
+
+// Order of a boundary state in the state buffer.  Handed from chunk to
+// chunk it follows the accumulator's lane order, tile after tile: tile
+// (nt, pt) is 64 pieces of 4 floats, piece l holding state[16 pt + l % 16]
+// [16 nt + 4 (l / 16) + 0..3], so a wave's load or store of a tile is 1 KB of
+// consecutive bytes.  The initial and the final state are row-major.
+template <int P>
+__device__ __forceinline__ int state_tile_off(int nt, int pt, int lane) {
+    return ((nt * (P / 16) + pt) * 64 + lane) * 16;
+}
+
 struct FwdParams {
     const void *x;
     const float *dt;
@@ -94,7 +108,7 @@ struct FwdParams {
     const float *init_state;  // may be null
     void *y;
     float *state;             // boundary-state buffer; holds the final state at the end
-    const int4 *chunks;       // {seq, chunk index in seq, first token, length}
+    const int4 *chunks;       // {seq, chunk index in seq, first token, length | kLastChunk on a sequence's last}
     const int *n_chunks;      // number of valid chunk entries
     int *tickets;             // one counter per XCD
     const int *items;         // per-XCD work-item lists, concatenated
@@ -463,7 +477,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
         const int seq = ce.x;
         const int cloc = ce.y;
         const long long tok0 = ce.z;
-        const int q = ce.w;
+        const int q = ce.w & (kLastChunk - 1);
+        const bool last = (ce.w & kLastChunk) != 0;
         const int xs = H * P;          // token stride of x and y (elements)
         const int bs = G * N;          // token stride of B and C
         const IO *Bg = reinterpret_cast<const IO *>(prm.B) + tok0 * bs + g * N;
@@ -776,7 +791,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                         const int nt = wn + a * S::WN, pt = wp + b * S::WP;
                         const bool ok = wp < S::PT && nt < S::NT && pt < S::PT;
                         hv[a][b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rin, ok ? ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4 : kPastEnd, 0, kStateLoad));
+                            rin, !ok ? kPastEnd : cloc == 0 ? ((pt * 16 + li) * N + nt * 16 + 4 * lg) * 4
+                                                            : state_tile_off<P>(nt, pt, li + 16 * lg), 0, kStateLoad));
                     }
             };
             load_state(early);
@@ -925,6 +941,16 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
             }
             const float alpha = exp2f_fast(s2_last);
             if constexpr (SSD_RACE_WIDEN != 0) race_widen_delay(unit, cloc, wave);
+            // A sequence's first and last chunks read and write the state in
+            // different orders (row-major in and tile order out, or the
+            // reverse), so one wave's stores could land on state that another
+            // wave has yet to read (when the initial state is the output
+            // buffer, or in the last chunk, always): every wave's state loads
+            // complete first.  Other chunks write exactly what each wave read.
+            if ((cloc == 0) != last) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+                __syncthreads();
+            }
             {
                 const __amdgpu_buffer_rsrc_t rout = buf_rsrc(hout, P * N * 4);
     #pragma unroll
@@ -943,7 +969,8 @@ __global__ __launch_bounds__(512) void ssd_fwd_kernel(FwdParams prm) {
                             hb[r] = from_f32<IO>(hv[a][b][r]);
                         }
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), rout,
-                                                               ok ? (p * N + n0) * 4 : kPastEnd, 0, 0);
+                                                               !ok ? kPastEnd : last ? (p * N + n0) * 4
+                                                                                    : state_tile_off<P>(nt, pt, li + 16 * lg), 0, 0);
                         if (ok) *reinterpret_cast<Half *>(sH + lds_off<IO, S::NP>(p, n0)) = hb;
                     }
             }

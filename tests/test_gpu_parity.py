@@ -353,6 +353,35 @@ def test_in_place_state_resume():
     assert torch.equal(y, ref_y) and torch.equal(st, ref_fin)
 
 
+@pytest.mark.parametrize("P,N,Q", [(64, 256, 128), (64, 128, 64), (32, 64, 128)])
+def test_boundary_chunks_read_and_write_the_state_buffer(P, N, Q):
+    """Sequences of one, two and three chunks (packed), with the initial
+    state given in its own buffer and then as the output buffer itself (in
+    place).  A sequence's first and last chunks read the state in one order
+    and write it in another; every sequence's outputs and final state are
+    checked against the oracle on each of three calls, and the in-place
+    results must equal the out-of-place ones bitwise."""
+    lens = [Q // 2, Q + 1, 2 * Q, 3 * Q - 5, Q + Q // 2, 2 * Q + 3]
+    inp = wl.make_inputs(1, sum(lens), 4, P, N, 2, io="bf16", seed=31, init_std=0.5, lengths=lens)
+    d = hp.to_device(inp, DEV)
+    y_ref, fin_ref = hp.oracle_fwd(inp, D=True)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    for call in range(3):
+        y, fin = _run(d, Q)
+        torch.cuda.synchronize()
+        yy, ff = hp.to_numpy64(y), hp.to_numpy64(fin)
+        for s in range(len(lens)):
+            tag = f"P{P} N{N} Q{Q} call {call} sequence {s} ({lens[s]} tokens)"
+            assert hp.rel_l2(yy[:, cu[s]:cu[s + 1]], y_ref[:, cu[s]:cu[s + 1]]) <= hp.TOL["bf16"], tag
+            assert hp.rel_l2(ff[s], fin_ref[s]) <= 1e-3, tag
+        st = d["init_state"].clone()
+        y2, fin2 = ssd.chunk_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk_len=Q,
+                                      init_state=st, final_state=st, cu_seqlens=d["cu_seqlens"])
+        torch.cuda.synchronize()
+        assert fin2.data_ptr() == st.data_ptr()
+        assert torch.equal(y2, y) and torch.equal(st, fin), f"in place, call {call}"
+
+
 def test_zero_step_keeps_state():
     inp = wl.make_inputs(1, 300, 2, 64, 128, 1, io="bf16", seed=25, init_std=1.0)
     inp["dt"][:] = 0.0
