@@ -611,7 +611,8 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
     }
 
     // one head's inputs in registers (loaded a head ahead; R issued later than
-    // the rest, so that the loads do not all queue behind one barrier)
+    // the rest, so that the loads do not all queue behind one barrier; the
+    // states, read once, non-temporal)
     bf16x8 xr[XV], dyr[XV];
     f32x4 hr[SV], rr[SV];
     float dtr = 0.f;
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         for (int k = 0; k < SV; ++k) {
             const int i = (tid + NTH * k) * 4;
             rr[k] = zero4();
-            if (i < 4 * SP4) rr[k] = *reinterpret_cast<const f32x4 *>(Rc + i);
+            if (i < 4 * SP4) rr[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Rc + i));
         }
     };
     auto load_head = [&](int h, bool with_r) {
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
         for (int k = 0; k < SV; ++k) {
             const int i = (tid + NTH * k) * 4;
             hr[k] = zero4();
-            if (i < 4 * SP4) hr[k] = *reinterpret_cast<const f32x4 *>(Hc + i);
+            if (i < 4 * SP4) hr[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Hc + i));
         }
         if (wave == 0) dtr = lane < q ? p.dt[(t0 + lane) * (H / p.hsub) + h / p.hsub] : 0.f;
         if (with_r) load_r(h);
@@ -984,14 +985,16 @@ __device__ __forceinline__ void scan_bf16_chain(const BwdParams &p, int unit, bf
                 : zero4();
     }
     // the workspace's states in the tile order of state_piece_pos (tile t, this
-    // lane's piece); the initial-state gradient row-major (null: no store)
+    // lane's piece), non-temporal: only the chunk kernel reads them, after this
+    // launch, and the L2 keeps the B or C rows a group's heads share instead;
+    // the initial-state gradient row-major (null: no store)
     auto store_state = [&](float *dst, bool row_major = false) {
         const __amdgpu_buffer_rsrc_t r = buf_rsrc(dst, dst ? PN * 4 : 0);
 #pragma unroll
         for (int k = 0; k < TPW; ++k)
             if (wave + 4 * k < TILES)
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, st[k]), r,
-                                                       row_major ? tile_off(k) : ((wave + 4 * k) * 64 + lane) * 16, 0, 0);
+                                                       row_major ? tile_off(k) : ((wave + 4 * k) * 64 + lane) * 16, 0, kStream);
     };
     if (MODE == 0) store_state(p.states + ((long long)(o + s) * p.H + h) * PN);
 
