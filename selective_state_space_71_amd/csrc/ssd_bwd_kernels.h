@@ -571,8 +571,8 @@ __global__ __launch_bounds__(NW * 64) void ssd_bwd_chunk_bf16_kernel(BwdParams p
     const long long PN = (long long)P * N;
     const bf16 *xg = reinterpret_cast<const bf16 *>(p.x), *dyg = reinterpret_cast<const bf16 *>(p.dy);
     bf16 *dxg = reinterpret_cast<bf16 *>(p.dx);
-    // dx rows of head hp from LDS, as whole 128-byte rows (the dx phase's
-    // lanes hold 8-byte pieces of 16 tokens)
+    // dx rows of head hp from LDS, written as whole rows (P * 2 bytes, in
+    // 16-byte pieces; the dx phase's lanes hold 8-byte pieces of 16 tokens)
     auto flush_dx = [&](int hp) {
         for (int i = threadIdx.x; i < Q * (P / 8); i += NTH) {
             const int j = i / (P / 8), c8 = (i % (P / 8)) * 8;
