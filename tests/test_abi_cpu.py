@@ -259,6 +259,10 @@ def test_bwd_workspace_size_query(lib):
     assert n64 > 0 and n128 > n64
     for io, N in ((ssd.SSD_BF16, 256), (ssd.SSD_F32, 256)):
         assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(dstate=N)), io) > 0
+    # the scans address a 64-token chunk of x, dy, B or C rows with 32-bit
+    # byte offsets: 2^22 channels of fp32-sized rows reach 2^30 bytes
+    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(nheads=65536 - 1)), ssd.SSD_BF16) > 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(_dims(nheads=65536)), ssd.SSD_BF16) == 0
 
 
 @pytest.mark.parametrize("case,expect", [
