@@ -23,6 +23,12 @@ LIB = os.path.join(PKG, "libssd.so")
 # race-widening debug build (SSD_RACE_WIDEN=1), used by tests/test_gpu_race.py
 RACE_LIB = os.path.join(PKG, "libssd_racewiden.so")
 SOURCES = ["ssd_api.hip", "ssd_fwd_bf16.hip", "ssd_fwd_f32.hip"]
+# Per-unit compiler options.  The bf16 forward kernel is scheduled for
+# instruction-level parallelism: measured 1.3-1.6 % faster at the 2.7B-layer
+# and packed shapes with the same registers and the same memory-operation
+# order around its hand-written waits.  (The backward's chunk kernel spills
+# under that schedule and is slower.)
+UNIT_FLAGS = {"ssd_fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 ARCH = "gfx950"
 
 
@@ -46,7 +52,7 @@ def common_flags():
 def _compile(src: str, race_widen: bool = False) -> str:
     sub = os.path.join(BUILD, "race") if race_widen else BUILD
     obj = os.path.join(sub, os.path.splitext(src)[0] + ".o")
-    extra = ["-DSSD_RACE_WIDEN=1"] if race_widen else []
+    extra = (["-DSSD_RACE_WIDEN=1"] if race_widen else []) + UNIT_FLAGS.get(src, [])
     cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
